@@ -1,0 +1,206 @@
+/*
+ * libfusednorm -- the fused epilogue that follows a tensor-parallel reduction,
+ * and the MiniMax-style QK RMSNorm, as hand-written HIP kernels for gfx950
+ * (MI355X), behind a C ABI.
+ *
+ * Pages this interface follows (cited by title and section):
+ *   [TS-TRITON]  lightseekorg--tokenspeed, tokenspeed_kernel/ops/communication/
+ *                triton.py, section "AMD Triton All-Reduce + RMSNorm"
+ *                (amd_allreduce_residual_rmsnorm_kernel and its dispatcher
+ *                allreduce_residual_rmsnorm / allreduce_residual_rmsnorm_can_run).
+ *   [TS-TRTLLM]  lightseekorg--tokenspeed, tokenspeed_kernel/thirdparty/cuda/
+ *                trtllm.py, sections "Pattern enums" (AllReduceFusionPattern),
+ *                "AllReduce fusion" (trtllm_allreduce_fusion), "AllGather
+ *                fusion" (the 128-wide FP8 block) and "MiniMax QK fused AR +
+ *                RMSNorm" (minimax_allreduce_rms_qk).
+ *   [VLLM-QK]    vLLM API docs, vllm.model_executor.layers.minimax_rms_norm.
+ *                rms_norm_tp (_minimax_qk_norm_tp_eager, _minimax_qk_var_kernel,
+ *                _minimax_rms_apply_kernel).
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are DEVICE pointers to row-major data. bf16 travels as
+ *     16-bit storage, FP8 as one byte per value in OCP E4M3 ("e4m3fn": bias 7,
+ *     largest finite 448, no infinities, S.1111.111 = NaN).
+ *   - The caller owns and allocates every buffer; the library allocates no
+ *     device or host memory, keeps no state between calls and never
+ *     synchronises. Work is enqueued on `stream` (a hipStream_t; NULL = the
+ *     default stream) on the current device; results are ready when that stream
+ *     reaches the work. Calls are thread-safe and reentrant.
+ *   - Every argument is validated before anything is launched; on any error
+ *     nothing is launched and nothing is written. T == 0 is valid and launches
+ *     nothing.
+ *   - bf16 outputs are rounded to nearest, ties to even. Arithmetic is fp32.
+ *   - Overlap: no output may overlap any input or another output, with one
+ *     exception: residual_out may be exactly residual_in (in-place update).
+ *     Partial overlaps that the library can detect from the address ranges are
+ *     rejected with FUSEDNORM_ERR_UNSUPPORTED.
+ *   - NaN or Inf inputs are outside the contract.
+ */
+#ifndef FUSEDNORM_H
+#define FUSEDNORM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FUSEDNORM_VERSION 10000 /* major*10000 + minor*100 + patch */
+#define FUSEDNORM_MAX_PARTIALS 16
+#define FUSEDNORM_MAX_HIDDEN 16384
+#define FUSEDNORM_FP8_GROUP 128
+
+typedef enum {
+    FUSEDNORM_OK = 0,
+    /* A required pointer is NULL, a count or size is out of range, eps is
+     * negative or not finite, or tp_world is inconsistent with var_in. The
+     * [TS-TRTLLM] wrappers assert on such arguments. */
+    FUSEDNORM_ERR_INVALID_ARGUMENT = 1,
+    /* Well-formed but outside what the kernels handle: widths not a multiple
+     * of 8 elements, H above FUSEDNORM_MAX_HIDDEN, pointers not 16-byte
+     * aligned, an FP8 group other than 128, partially overlapping buffers. The
+     * [TS-TRITON] dispatcher returns (None, None, None, None) for unsupported
+     * inputs so the caller can take another path; this code plays that role. */
+    FUSEDNORM_ERR_UNSUPPORTED = 2,
+    /* The HIP runtime reported an error when the kernel was enqueued. */
+    FUSEDNORM_ERR_HIP = 3
+} fusednorm_status;
+
+/*
+ * fused_add_rmsnorm -- pattern kARResidualRMSNorm ([TS-TRTLLM] "Pattern enums";
+ * the computation is [TS-TRITON] amd_allreduce_residual_rmsnorm_kernel with the
+ * P peer buffers already resident in this GPU's memory).
+ *
+ * For every token t < T and channel j < H:
+ *   x[t,j]            = ((0 + p_0[t,j]) + p_1[t,j] + ... + p_{P-1}[t,j]) + residual_in[t,j]
+ *                       (fp32 accumulation in partial order 0..P-1, then the residual)
+ *   residual_out[t,j] = bf16(x[t,j])
+ *   norm_out[t,j]     = bf16( x[t,j] * rsqrt(mean_j(x[t,:]^2) + eps) * weight[j] )
+ * The mean uses the fp32 x, not bf16(x), and divides by the true H.
+ *
+ *   partials      HOST array of P device pointers, each bf16 [T, H], 16-B aligned
+ *   P             1 .. FUSEDNORM_MAX_PARTIALS
+ *   residual_in   bf16 [T, H]
+ *   weight        bf16 [H] per-channel RMSNorm weight (used as w, not 1 + w)
+ *   T, H          tokens (>= 0) and hidden width (8 .. 16384, multiple of 8)
+ *   eps           >= 0, added to the mean of squares inside the rsqrt
+ *   norm_out      bf16 [T, H], required
+ *   residual_out  bf16 [T, H], required; may equal residual_in
+ *   stream        hipStream_t or NULL
+ * Returns a fusednorm_status.
+ */
+int fused_add_rmsnorm(const void* const* partials, int P, const void* residual_in,
+                      const void* weight, int64_t T, int64_t H, float eps,
+                      void* norm_out, void* residual_out, void* stream);
+
+/*
+ * fused_add_rmsnorm_quant_fp8 -- pattern kARResidualRMSNormFP8Quant (with
+ * norm_out != NULL it also covers kARResidualRMSNormOutFP8Quant), [TS-TRTLLM]
+ * "Pattern enums". The fused epilogue above, then dynamic per-token FP8:
+ *   y[t,j]         = x[t,j] * rsqrt(mean_j(x[t,:]^2) + eps) * weight[j]   (fp32)
+ *   amax[t]        = max_j |y[t,j]|
+ *   scale_out[t]   = amax[t] / 448        (dequantisation multiplier: y ~ code * scale)
+ *   quant_out[t,j] = e4m3( clamp(y[t,j] / scale_out[t], -448, 448) ), nearest, ties to even
+ * The fp32 y is quantised, never bf16(y). A token whose amax is 0 gets scale 0
+ * and all codes 0x00.
+ *
+ *   norm_out      bf16 [T, H] or NULL (not written)
+ *   residual_out  bf16 [T, H], required; may equal residual_in
+ *   quant_out     e4m3 [T, H], 16-B aligned, required
+ *   scale_out     fp32 [T], 4-B aligned, required
+ * Other arguments as for fused_add_rmsnorm.
+ */
+int fused_add_rmsnorm_quant_fp8(const void* const* partials, int P, const void* residual_in,
+                                const void* weight, int64_t T, int64_t H, float eps,
+                                void* norm_out, void* residual_out, void* quant_out,
+                                float* scale_out, void* stream);
+
+/*
+ * fused_add_rmsnorm_quant_fp8_block -- pattern kARResidualRMSNormFP8BlockWiseQuant
+ * ([TS-TRTLLM] "Pattern enums"; the 128-wide block from "AllGather fusion").
+ * As fused_add_rmsnorm_quant_fp8, but with one scale per group g of
+ * group_size consecutive channels of a token:
+ *   amax[t,g]          = max_{j in [g*128, g*128+128)} |y[t,j]|
+ *   scale_out[t,g]     = amax[t,g] / 448
+ *   quant_out[t,j]     = e4m3( clamp(y[t,j] / scale_out[t,g], -448, 448) )
+ *
+ *   group_size    must be FUSEDNORM_FP8_GROUP (128); H must be a multiple of it
+ *   scale_out     fp32 [T, H/128] row-major, 4-B aligned, required
+ * Other arguments as for fused_add_rmsnorm_quant_fp8.
+ */
+int fused_add_rmsnorm_quant_fp8_block(const void* const* partials, int P,
+                                      const void* residual_in, const void* weight, int64_t T,
+                                      int64_t H, float eps, int group_size, void* norm_out,
+                                      void* residual_out, void* quant_out, float* scale_out,
+                                      void* stream);
+
+/*
+ * qk_rmsnorm -- the MiniMax QK RMSNorm under tensor parallelism ([VLLM-QK]
+ * _minimax_qk_norm_tp_eager and _minimax_rms_apply_kernel; [TS-TRTLLM]
+ * minimax_allreduce_rms_qk for the contiguous outputs).
+ *
+ * Token t's row starts at qkv + t * row_stride and holds q (q_size elements),
+ * then k (kv_size), then v (kv_size; never read or written). Per token:
+ *   var_q, var_k = var_in[t,0], var_in[t,1]           if var_in != NULL
+ *                = mean(q^2), mean(k^2) (fp32)         if var_in == NULL (tp_world must be 1)
+ *   q_out[t,:] = bf16( q * rsqrt(var_q / tp_world + eps) * q_weight )
+ *   k_out[t,:] = bf16( k * rsqrt(var_k / tp_world + eps) * k_weight )
+ * var_in holds, per token, the sum over tp_world shards of each shard's local
+ * mean of squares (what the all-reduce of qk_rmsnorm_var's output yields), so
+ * var / tp_world is the mean over the whole row.
+ *
+ *   qkv           bf16, 16-B aligned; row_stride (elements) a multiple of 8 and
+ *                 >= q_size + kv_size
+ *   T             tokens (>= 0)
+ *   q_size        multiple of 8, > 0;  kv_size multiple of 8, > 0;
+ *                 q_size + kv_size <= 16384
+ *   q_weight      bf16 [q_size];  k_weight bf16 [kv_size]
+ *   eps           >= 0
+ *   tp_world      >= 1
+ *   var_in        fp32 [T, 2], 8-B aligned, or NULL
+ *   q_out         bf16 [T, q_size] contiguous;  k_out bf16 [T, kv_size] contiguous
+ */
+int qk_rmsnorm(const void* qkv, int64_t T, int64_t row_stride, int64_t q_size,
+               int64_t kv_size, const void* q_weight, const void* k_weight, float eps,
+               int tp_world, const float* var_in, void* q_out, void* k_out, void* stream);
+
+/*
+ * qk_rmsnorm_var -- the tensor-parallel "pre" stage of the QK norm ([VLLM-QK]
+ * _minimax_qk_var_kernel): per token, the local means of squares of the q and k
+ * segments, accumulated in fp32:
+ *   var_out[t,0] = mean(q^2),  var_out[t,1] = mean(k^2)
+ * Summing var_out over the shards of a row (the all-reduce, not part of this
+ * library) gives qk_rmsnorm's var_in.
+ *
+ *   var_out       fp32 [T, 2], 8-B aligned
+ * Other arguments as for qk_rmsnorm.
+ */
+int qk_rmsnorm_var(const void* qkv, int64_t T, int64_t row_stride, int64_t q_size,
+                   int64_t kv_size, float* var_out, void* stream);
+
+/*
+ * fusednorm_e4m3_encode -- element-wise fp32 -> OCP E4M3 with exactly the
+ * conversion the FP8 epilogues use (clamp to [-448, 448], round to nearest,
+ * ties to even, sign kept, so a negative value that rounds to zero is 0x80).
+ * It exposes that conversion so it can be checked on its own.
+ *
+ *   in    fp32 [n], 16-B aligned;  out  uint8 [n], 16-B aligned;  n >= 0
+ */
+int fusednorm_e4m3_encode(const float* in, void* out, int64_t n, void* stream);
+
+/* Static description of a status code. Never NULL. */
+const char* fusednorm_status_string(int status);
+
+/* Detail of the last non-OK status returned on the calling thread (which
+ * argument failed which check); "" when there is none. Valid until the next
+ * call on that thread. */
+const char* fusednorm_last_error(void);
+
+/* FUSEDNORM_VERSION of the built library. */
+int fusednorm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FUSEDNORM_H */
