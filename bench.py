@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Throughput of the fused TP epilogue and the QK RMSNorm on one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic input:
+  1. fused_add_rmsnorm_quant_fp8        prefill, T=8192 H=8192 P=8, per-token e4m3
+  2. qk_rmsnorm (local means)           MiniMax QK, T=4096, row 8192 = q 6144 | k 1024 | v
+  3. fused_add_rmsnorm_quant_fp8_block  T=16384 H=7168 P=2, 1x128 e4m3 groups
+  4. qk_rmsnorm (sum of 4 shard means)  as 2, tp_world=4
+The launches alternate between the large FP8 passes (>= 1 GB each) and the QK
+passes, so no launch finds its inputs in the 256 MB last-level cache.
+
+Prints ONE JSON line. ``value`` is the step's algorithmic bytes (each input
+read once, each output written once, weights once per launch) divided by the
+wall time of a step, in GB/s; ``roofline`` is the dominant kernel (the
+per-token FP8 epilogue) timed with HIP events on its launch stream;
+``cpu_baseline`` times the CPU oracle on one full step of the same inputs.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published peak
+KERNEL_SRC = os.path.join(ROOT, "residual_add_rmsnorm_amd", "csrc", "fusednorm_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_fp8_token.json")
+STEP = ["prefill_fp8_token", "qk_local", "fp8_block", "qk_sharded"]
+DOMINANT = "prefill_fp8_token"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the CPU oracle leg (for profiler runs)")
+    ap.add_argument("--out", default=None, help="also write the JSON line to this file")
+    return ap.parse_args()
+
+
+def source_digest() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None when it is missing or was taken on other kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != source_digest():
+        return None
+    return t.get("bytes_per_launch")
+
+
+class Part:
+    """One launch of the step: inputs resident on the GPU, outputs allocated."""
+
+    def __init__(self, name, fn, wl, torch, dev):
+        self.name = name
+        self.w = w = wl.WORKLOADS[name]
+        t0 = time.perf_counter()
+        self.cpu = wl.make_inputs(w)
+        if w.kind == "qk":
+            self.qkv = self.cpu.qkv.to(dev)
+            self.wq = self.cpu.q_weight.to(dev)
+            self.wk = self.cpu.k_weight.to(dev)
+            self.q_out = torch.empty(w.T, w.q_size, dtype=torch.bfloat16, device=dev)
+            self.k_out = torch.empty(w.T, w.kv_size, dtype=torch.bfloat16, device=dev)
+            self.var_in = None
+            if w.tp_world > 1:
+                # Each shard's local means (the pre stage), summed as the
+                # all-reduce between the two stages would; prepared once, untimed.
+                shards = [self.qkv] + [s.to(dev) for s in self.cpu.shards]
+                self.var_in = sum(fn.qk_rmsnorm_var(s, w.q_size, w.kv_size) for s in shards)
+                del shards
+            self.call = lambda: fn.qk_rmsnorm(self.qkv, w.q_size, w.kv_size, self.wq, self.wk,
+                                              w.eps, w.tp_world, self.var_in, self.q_out,
+                                              self.k_out)
+        else:
+            self.parts = [p.to(dev) for p in self.cpu.partials]
+            self.res = self.cpu.residual.to(dev)
+            self.weight = self.cpu.weight.to(dev)
+            self.res_out = torch.empty_like(self.res)
+            self.quant = torch.empty(w.T, w.H, dtype=torch.float8_e4m3fn, device=dev)
+            if w.kind == "quant_token":
+                self.scale = torch.empty(w.T, dtype=torch.float32, device=dev)
+                f = fn.fused_add_rmsnorm_quant_fp8
+            else:
+                self.scale = torch.empty(w.T, w.H // w.group_size, dtype=torch.float32,
+                                         device=dev)
+                f = fn.fused_add_rmsnorm_quant_fp8_block
+            self.call = lambda: f(self.parts, self.res, self.weight, w.eps, None, self.res_out,
+                                  self.quant, self.scale)
+        self.bytes = w.algorithmic_bytes()
+        log(f"[bench] {name}: {w.description}; {self.bytes / 1e6:.1f} MB per launch "
+            f"(inputs drawn in {time.perf_counter() - t0:.1f} s)")
+
+
+def cpu_baseline(parts):
+    """The oracle, untuned, on one full step of the same host-resident inputs."""
+    import numpy as np
+
+    import oracle
+    from residual_add_rmsnorm_amd import workloads as wl
+
+    total_bytes, total_s = 0, 0.0
+    for p in parts:
+        w = p.w
+        if w.kind == "qk":
+            rows = wl.bits(p.cpu.qkv)
+            var = None if p.var_in is None else p.var_in.cpu().numpy().astype(np.float32)
+            t0 = time.perf_counter()
+            oracle.qk_rmsnorm(rows, w.q_size, w.kv_size, wl.bits(p.cpu.q_weight),
+                              wl.bits(p.cpu.k_weight), w.eps, w.tp_world, var)
+        else:
+            args = ([wl.bits(x) for x in p.cpu.partials], wl.bits(p.cpu.residual),
+                    wl.bits(p.cpu.weight), w.eps)
+            t0 = time.perf_counter()
+            oracle.fused_add_rmsnorm(*args, quant="token" if w.kind == "quant_token" else "block",
+                                     want_norm=False)
+        dt = time.perf_counter() - t0
+        log(f"[bench] cpu oracle {p.name}: {dt:.2f} s")
+        total_bytes += p.bytes
+        total_s += dt
+    return {"value": round(total_bytes / total_s / 1e9, 3), "unit": "GB/s",
+            "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": "one full step (all four launches, every token) on the host, "
+                      f"{total_s:.1f} s"}
+
+
+def copy_ceiling(torch, dev):
+    """GB/s of a plain device-to-device copy of 1 GiB (read + write counted)."""
+    n = 1 << 29
+    src = torch.empty(n, dtype=torch.bfloat16, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    reps = 10
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    sec = a.elapsed_time(b) / 1e3 / reps
+    del src, dst
+    return round(2 * n * 2 / sec / 1e9, 1)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE={world}); the multi-GPU exchange is not built, so there is no "
+              "figure at more than one GPU.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from residual_add_rmsnorm_amd import fusednorm as fn
+    from residual_add_rmsnorm_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] {torch.cuda.get_device_name(dev)}; library {fn.library_path()}")
+    parts = [Part(n, fn, wl, torch, dev) for n in STEP]
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        for p in parts:
+            p.call()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = {p.name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(K)] for p in parts}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        for p in parts:
+            s, e = ev[p.name][k]
+            s.record()
+            p.call()
+            e.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    step_bytes = sum(p.bytes for p in parts)
+    step_tokens = sum(p.w.T for p in parts)
+    ms_per_step = wall / K * 1e3
+    per = {}
+    for p in parts:
+        us = sum(s.elapsed_time(e) for s, e in ev[p.name]) / K * 1e3
+        per[p.name] = {"us": round(us, 2), "GB/s": round(p.bytes / us / 1e3, 1),
+                       "frac": round(p.bytes / us / 1e3 / HBM_PEAK_GBS, 4),
+                       "tokens/s": round(p.w.T / us * 1e6)}
+        log(f"[bench] {p.name}: {us:.1f} us, {per[p.name]['GB/s']} GB/s "
+            f"({100 * per[p.name]['frac']:.1f}% of {HBM_PEAK_GBS:.0f})")
+    dom = next(p for p in parts if p.name == DOMINANT)
+    dom_gbs = per[DOMINANT]["GB/s"]
+    traffic = measured_traffic()
+
+    result = {
+        "metric": "achieved HBM GB/s (% of MI355X peak) and tokens/s, fused add+RMSNorm(+FP8)",
+        "value": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded CPU draws, bf16 inputs resident in HBM)",
+        "config": {
+            "workload": "fused TP epilogue step: prefill per-token e4m3 T=8192 H=8192 P=8 + "
+                        "MiniMax QK T=4096 local means + block e4m3 T=16384 H=7168 P=2 + "
+                        "MiniMax QK T=4096 with 4 shard means",
+            "launches": STEP,
+            "bytes_per_step": step_bytes,
+            "tokens_per_step": step_tokens,
+            "storage": "bf16 in; bf16 and OCP e4m3 out",
+            "parallelism": "single GPU",
+        },
+        "pct_of_peak": round(100 * step_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(step_tokens / (ms_per_step / 1e3)),
+        "per_launch": per,
+        "roofline": {
+            "bound": "hbm", "kernel": "fused_epilogue_kernel (per-token e4m3)",
+            "achieved": dom_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": dom.bytes,
+        },
+        "copy_ceiling_GBs": copy_ceiling(torch, dev),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(parts)
+    line = json.dumps(result)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(line + "\n")
+    print(line, flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -27,14 +27,17 @@
  *     default stream) on the current device; results are ready when that stream
  *     reaches the work. Calls are thread-safe and reentrant.
  *   - Every argument is validated before anything is launched; on any error
- *     nothing is launched and nothing is written. T == 0 is valid and launches
+ *     nothing is launched and nothing is written. T == 0 (n == 0) is valid:
+ *     once the scalar arguments are checked the call returns FUSEDNORM_OK
+ *     without examining any buffer (empty tensors may pass NULL) and launches
  *     nothing.
  *   - bf16 outputs are rounded to nearest, ties to even. Arithmetic is fp32.
  *   - Overlap: no output may overlap any input or another output, with one
  *     exception: residual_out may be exactly residual_in (in-place update).
  *     Partial overlaps that the library can detect from the address ranges are
  *     rejected with FUSEDNORM_ERR_UNSUPPORTED.
- *   - NaN or Inf inputs are outside the contract.
+ *   - NaN or Inf inputs are outside the contract. With eps == 0 an all-zero
+ *     token has no defined norm (0 * rsqrt(0)) and its outputs are NaN.
  */
 #ifndef FUSEDNORM_H
 #define FUSEDNORM_H

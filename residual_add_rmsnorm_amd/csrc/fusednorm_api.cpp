@@ -1,0 +1,330 @@
+// C-ABI entry points of libfusednorm (declared in include/fusednorm.h).
+//
+// Every argument is checked on the host before anything touches the HIP
+// runtime, so invalid calls return a status without launching or writing
+// anything, also on a machine without a GPU. The checks mirror the pages'
+// supported-input contract: the tokenspeed triton.py page, section "AMD Triton
+// All-Reduce + RMSNorm" (allreduce_residual_rmsnorm_can_run: bf16, contiguous,
+// 2-D, matching shapes; the dispatcher returns no result for unsupported
+// inputs) and the 128-element FP8 block of the tokenspeed trtllm.py page,
+// section "AllGather fusion".
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include <hip/hip_runtime.h>
+
+#include "fusednorm.h"
+#include "fusednorm_internal.h"
+
+namespace {
+
+using fusednorm::u32x2;
+using fusednorm::u32x4;
+
+thread_local char g_last_error[256] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_last_error[0] = '\0';
+    return FUSEDNORM_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Byte range [lo, hi) of a buffer.
+struct Span {
+    uintptr_t lo, hi;
+    const char* name;
+};
+
+Span span(const void* p, int64_t bytes, const char* name) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Span{lo, lo + (uintptr_t)(bytes > 0 ? bytes : 0), name};
+}
+
+bool intersects(const Span& a, const Span& b) {
+    return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+// Outputs must not overlap inputs or each other. The one allowed alias is an
+// input and an output that are the same buffer exactly (`same_ok` pairs).
+int check_overlaps(const Span* in, int n_in, const Span* out, int n_out, int alias_in,
+                   int alias_out) {
+    for (int o = 0; o < n_out; ++o) {
+        for (int i = 0; i < n_in; ++i) {
+            if (!intersects(out[o], in[i])) continue;
+            if (i == alias_in && o == alias_out && out[o].lo == in[i].lo && out[o].hi == in[i].hi)
+                continue;
+            return fail(FUSEDNORM_ERR_UNSUPPORTED, "%s overlaps %s", out[o].name, in[i].name);
+        }
+        for (int p = o + 1; p < n_out; ++p)
+            if (intersects(out[o], out[p]))
+                return fail(FUSEDNORM_ERR_UNSUPPORTED, "%s overlaps %s", out[o].name, out[p].name);
+    }
+    return FUSEDNORM_OK;
+}
+
+int check_eps(float eps) {
+    if (!(eps >= 0.0f) || !isfinite(eps))
+        return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+    return FUSEDNORM_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess)
+        return fail(FUSEDNORM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+enum class Quant { None, Token, Block };
+
+int fused_common(const void* const* partials, int P, const void* residual_in, const void* weight,
+                 int64_t T, int64_t H, float eps, int group_size, void* norm_out,
+                 void* residual_out, void* quant_out, float* scale_out, void* stream, Quant quant) {
+    // ---- scalar arguments
+    if (P < 1 || P > FUSEDNORM_MAX_PARTIALS)
+        return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "P = %d outside [1, %d]", P,
+                    FUSEDNORM_MAX_PARTIALS);
+    if (T < 0) return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "T = %lld < 0", (long long)T);
+    if (H <= 0) return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "H = %lld <= 0", (long long)H);
+    if (int s = check_eps(eps)) return s;
+    if (H % 8 != 0)
+        return fail(FUSEDNORM_ERR_UNSUPPORTED, "H = %lld is not a multiple of 8", (long long)H);
+    if (H > FUSEDNORM_MAX_HIDDEN)
+        return fail(FUSEDNORM_ERR_UNSUPPORTED, "H = %lld above %d", (long long)H,
+                    FUSEDNORM_MAX_HIDDEN);
+    if (T > 0x7FFFFFFF) return fail(FUSEDNORM_ERR_UNSUPPORTED, "T above 2^31 - 1");
+    if (quant == Quant::Block) {
+        if (group_size != FUSEDNORM_FP8_GROUP)
+            return fail(FUSEDNORM_ERR_UNSUPPORTED, "group_size = %d (only %d)", group_size,
+                        FUSEDNORM_FP8_GROUP);
+        if (H % FUSEDNORM_FP8_GROUP != 0)
+            return fail(FUSEDNORM_ERR_UNSUPPORTED, "H = %lld is not a multiple of %d",
+                        (long long)H, FUSEDNORM_FP8_GROUP);
+    }
+    if (T == 0) return ok();  // nothing to read or write: buffers are not examined
+    // ---- buffers
+    if (!partials) return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "partials is NULL");
+    for (int p = 0; p < P; ++p)
+        if (!partials[p]) return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "partials[%d] is NULL", p);
+    if (!residual_in) return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "residual_in is NULL");
+    if (!weight) return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "weight is NULL");
+    if (!residual_out) return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "residual_out is NULL");
+    if (quant == Quant::None && !norm_out)
+        return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "norm_out is NULL");
+    if (quant != Quant::None && !quant_out)
+        return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "quant_out is NULL");
+    if (quant != Quant::None && !scale_out)
+        return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "scale_out is NULL");
+    for (int p = 0; p < P; ++p)
+        if (!aligned(partials[p], 16))
+            return fail(FUSEDNORM_ERR_UNSUPPORTED, "partials[%d] not 16-byte aligned", p);
+    if (!aligned(residual_in, 16)) return fail(FUSEDNORM_ERR_UNSUPPORTED, "residual_in not 16-byte aligned");
+    if (!aligned(weight, 16)) return fail(FUSEDNORM_ERR_UNSUPPORTED, "weight not 16-byte aligned");
+    if (!aligned(residual_out, 16)) return fail(FUSEDNORM_ERR_UNSUPPORTED, "residual_out not 16-byte aligned");
+    if (norm_out && !aligned(norm_out, 16)) return fail(FUSEDNORM_ERR_UNSUPPORTED, "norm_out not 16-byte aligned");
+    if (quant_out && !aligned(quant_out, 16)) return fail(FUSEDNORM_ERR_UNSUPPORTED, "quant_out not 16-byte aligned");
+    if (scale_out && !aligned(scale_out, 4)) return fail(FUSEDNORM_ERR_UNSUPPORTED, "scale_out not 4-byte aligned");
+    // ---- buffer overlap
+    const int64_t row_bytes = H * 2;
+    Span in[FUSEDNORM_MAX_PARTIALS + 2];
+    int n_in = 0;
+    for (int p = 0; p < P; ++p) in[n_in++] = span(partials[p], T * row_bytes, "a partial");
+    const int residual_idx = n_in;
+    in[n_in++] = span(residual_in, T * row_bytes, "residual_in");
+    in[n_in++] = span(weight, row_bytes, "weight");
+    Span out[4];
+    int n_out = 0;
+    out[n_out++] = span(residual_out, T * row_bytes, "residual_out");
+    if (norm_out) out[n_out++] = span(norm_out, T * row_bytes, "norm_out");
+    if (quant != Quant::None) {
+        out[n_out++] = span(quant_out, T * H, "quant_out");
+        const int64_t scales = quant == Quant::Token ? T : T * (H / FUSEDNORM_FP8_GROUP);
+        out[n_out++] = span(scale_out, scales * 4, "scale_out");
+    }
+    if (int s = check_overlaps(in, n_in, out, n_out, residual_idx, 0)) return s;
+
+    // ---- launch
+    fusednorm::EpilogueArgs a{};
+    for (int p = 0; p < P; ++p) a.partials[p] = static_cast<const u32x4*>(partials[p]);
+    a.residual = static_cast<const u32x4*>(residual_in);
+    a.weight = static_cast<const u32x4*>(weight);
+    a.residual_out = static_cast<u32x4*>(residual_out);
+    a.norm_out = static_cast<u32x4*>(norm_out);
+    a.quant_out = static_cast<u32x2*>(quant_out);
+    a.scale_out = scale_out;
+    a.P = P;
+    a.nvec = (int)(H / 8);
+    a.groups = (int)(H / FUSEDNORM_FP8_GROUP);
+    a.h = (float)H;
+    a.eps = eps;
+    const fusednorm::EpilogueMode mode = quant == Quant::None    ? fusednorm::kModeNorm
+                                         : quant == Quant::Token ? fusednorm::kModeQuantToken
+                                                                 : fusednorm::kModeQuantBlock;
+    const fusednorm::LaunchShape shape = fusednorm::pick_shape(a.nvec);
+    (void)hipGetLastError();  // start from a clean error state
+    return hip_status(fusednorm::launch_epilogue(a, mode, T, shape, (hipStream_t)stream),
+                      "kernel launch");
+}
+
+int qk_common(const void* qkv, int64_t T, int64_t row_stride, int64_t q_size, int64_t kv_size,
+              const void* q_weight, const void* k_weight, float eps, int tp_world,
+              const float* var_in, void* q_out, void* k_out, float* var_out, void* stream,
+              fusednorm::QkMode mode) {
+    const bool stats = mode == fusednorm::kQkStats;
+    if (T < 0) return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "T = %lld < 0", (long long)T);
+    if (q_size <= 0 || kv_size <= 0)
+        return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "q_size and kv_size must be > 0");
+    if (row_stride <= 0) return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "row_stride must be > 0");
+    if (!stats) {
+        if (int s = check_eps(eps)) return s;
+        if (tp_world < 1) return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "tp_world = %d < 1", tp_world);
+        if (!var_in && tp_world != 1)
+            return fail(FUSEDNORM_ERR_INVALID_ARGUMENT,
+                        "tp_world = %d needs var_in (the sum of the shards' means)", tp_world);
+    }
+    if (q_size % 8 || kv_size % 8 || row_stride % 8)
+        return fail(FUSEDNORM_ERR_UNSUPPORTED, "q_size, kv_size and row_stride must be multiples of 8");
+    if (row_stride < q_size + kv_size)
+        return fail(FUSEDNORM_ERR_UNSUPPORTED, "row_stride %lld < q_size + kv_size", (long long)row_stride);
+    if (q_size + kv_size > FUSEDNORM_MAX_HIDDEN)
+        return fail(FUSEDNORM_ERR_UNSUPPORTED, "q_size + kv_size above %d", FUSEDNORM_MAX_HIDDEN);
+    if (T > 0x7FFFFFFF) return fail(FUSEDNORM_ERR_UNSUPPORTED, "T above 2^31 - 1");
+    if (T == 0) return ok();  // nothing to read or write: buffers are not examined
+    if (!qkv) return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "qkv is NULL");
+    if (stats) {
+        if (!var_out) return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "var_out is NULL");
+    } else {
+        if (!q_weight || !k_weight)
+            return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "q_weight / k_weight is NULL");
+        if (!q_out || !k_out) return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "q_out / k_out is NULL");
+    }
+    if (!aligned(qkv, 16)) return fail(FUSEDNORM_ERR_UNSUPPORTED, "qkv not 16-byte aligned");
+    if (!stats) {
+        if (!aligned(q_weight, 16) || !aligned(k_weight, 16))
+            return fail(FUSEDNORM_ERR_UNSUPPORTED, "q_weight / k_weight not 16-byte aligned");
+        if (!aligned(q_out, 16) || !aligned(k_out, 16))
+            return fail(FUSEDNORM_ERR_UNSUPPORTED, "q_out / k_out not 16-byte aligned");
+        if (var_in && !aligned(var_in, 8))
+            return fail(FUSEDNORM_ERR_UNSUPPORTED, "var_in not 8-byte aligned");
+    } else if (!aligned(var_out, 8)) {
+        return fail(FUSEDNORM_ERR_UNSUPPORTED, "var_out not 8-byte aligned");
+    }
+    const int64_t qkv_bytes = ((T - 1) * row_stride + q_size + kv_size) * 2;
+    Span in[4];
+    int n_in = 0;
+    in[n_in++] = span(qkv, qkv_bytes, "qkv");
+    Span out[2];
+    int n_out = 0;
+    if (stats) {
+        out[n_out++] = span(var_out, T * 8, "var_out");
+    } else {
+        in[n_in++] = span(q_weight, q_size * 2, "q_weight");
+        in[n_in++] = span(k_weight, kv_size * 2, "k_weight");
+        if (var_in) in[n_in++] = span(var_in, T * 8, "var_in");
+        out[n_out++] = span(q_out, T * q_size * 2, "q_out");
+        out[n_out++] = span(k_out, T * kv_size * 2, "k_out");
+    }
+    if (int s = check_overlaps(in, n_in, out, n_out, -1, -1)) return s;
+
+    fusednorm::QkArgs a{};
+    a.qkv = static_cast<const uint16_t*>(qkv);
+    a.row_stride = row_stride;
+    a.wq = static_cast<const u32x4*>(q_weight);
+    a.wk = static_cast<const u32x4*>(k_weight);
+    a.q_out = static_cast<u32x4*>(q_out);
+    a.k_out = static_cast<u32x4*>(k_out);
+    a.var_in = reinterpret_cast<const float2*>(var_in);
+    a.var_out = reinterpret_cast<float2*>(var_out);
+    a.nq = (int)(q_size / 8);
+    a.nk = (int)(kv_size / 8);
+    a.q_size = (float)q_size;
+    a.kv_size = (float)kv_size;
+    a.tp_world = (float)tp_world;
+    a.eps = eps;
+    if (!stats) mode = var_in ? fusednorm::kQkSupplied : fusednorm::kQkLocal;
+    const fusednorm::LaunchShape shape = fusednorm::pick_shape(a.nq + a.nk);
+    (void)hipGetLastError();
+    return hip_status(fusednorm::launch_qk(a, mode, T, shape, (hipStream_t)stream), "kernel launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int fused_add_rmsnorm(const void* const* partials, int P, const void* residual_in,
+                      const void* weight, int64_t T, int64_t H, float eps, void* norm_out,
+                      void* residual_out, void* stream) {
+    return fused_common(partials, P, residual_in, weight, T, H, eps, 0, norm_out, residual_out,
+                        nullptr, nullptr, stream, Quant::None);
+}
+
+int fused_add_rmsnorm_quant_fp8(const void* const* partials, int P, const void* residual_in,
+                                const void* weight, int64_t T, int64_t H, float eps,
+                                void* norm_out, void* residual_out, void* quant_out,
+                                float* scale_out, void* stream) {
+    return fused_common(partials, P, residual_in, weight, T, H, eps, 0, norm_out, residual_out,
+                        quant_out, scale_out, stream, Quant::Token);
+}
+
+int fused_add_rmsnorm_quant_fp8_block(const void* const* partials, int P,
+                                      const void* residual_in, const void* weight, int64_t T,
+                                      int64_t H, float eps, int group_size, void* norm_out,
+                                      void* residual_out, void* quant_out, float* scale_out,
+                                      void* stream) {
+    return fused_common(partials, P, residual_in, weight, T, H, eps, group_size, norm_out,
+                        residual_out, quant_out, scale_out, stream, Quant::Block);
+}
+
+int qk_rmsnorm(const void* qkv, int64_t T, int64_t row_stride, int64_t q_size, int64_t kv_size,
+               const void* q_weight, const void* k_weight, float eps, int tp_world,
+               const float* var_in, void* q_out, void* k_out, void* stream) {
+    return qk_common(qkv, T, row_stride, q_size, kv_size, q_weight, k_weight, eps, tp_world,
+                     var_in, q_out, k_out, nullptr, stream, fusednorm::kQkLocal);
+}
+
+int qk_rmsnorm_var(const void* qkv, int64_t T, int64_t row_stride, int64_t q_size,
+                   int64_t kv_size, float* var_out, void* stream) {
+    return qk_common(qkv, T, row_stride, q_size, kv_size, nullptr, nullptr, 0.0f, 1, nullptr,
+                     nullptr, nullptr, var_out, stream, fusednorm::kQkStats);
+}
+
+int fusednorm_e4m3_encode(const float* in, void* out, int64_t n, void* stream) {
+    if (n < 0) return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "n < 0");
+    if (n == 0) return ok();
+    if (!in || !out) return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "in / out is NULL");
+    if (!aligned(in, 16) || !aligned(out, 16))
+        return fail(FUSEDNORM_ERR_UNSUPPORTED, "in / out not 16-byte aligned");
+    const Span i = span(in, n * 4, "in"), o = span(out, n, "out");
+    if (int s = check_overlaps(&i, 1, &o, 1, -1, -1)) return s;
+    if ((n + 7) / 8 > (int64_t)0x7FFFFFFF * 256) return fail(FUSEDNORM_ERR_UNSUPPORTED, "n too large");
+    (void)hipGetLastError();
+    return hip_status(fusednorm::launch_e4m3_encode(in, static_cast<uint8_t*>(out), n,
+                                                    (hipStream_t)stream),
+                      "kernel launch");
+}
+
+const char* fusednorm_status_string(int status) {
+    switch (status) {
+        case FUSEDNORM_OK: return "ok";
+        case FUSEDNORM_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case FUSEDNORM_ERR_UNSUPPORTED: return "unsupported input";
+        case FUSEDNORM_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* fusednorm_last_error(void) { return g_last_error; }
+
+int fusednorm_version(void) { return FUSEDNORM_VERSION; }
+
+}  // extern "C"

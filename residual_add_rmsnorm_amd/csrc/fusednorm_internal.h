@@ -1,0 +1,73 @@
+// Internal declarations shared by the kernels and the C-ABI layer of
+// libfusednorm. Not installed; the public interface is include/fusednorm.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fusednorm {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 8 bf16 = 16 bytes
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));  // 8 e4m3 codes = 8 bytes
+
+constexpr int kWave = 64;
+constexpr int kMaxWaves = 16;   // 1024 threads per workgroup
+constexpr int kMaxPartials = 16;
+constexpr int kMaxVpt = 8;      // 16-byte vectors per lane per token
+
+// Largest workgroup each vectors-per-lane variant is compiled for: more
+// vectors per lane hold more loads in flight and need more VGPRs, so fewer
+// waves may share a CU.
+constexpr __host__ __device__ int max_threads_for(int vpt) {
+    return vpt <= 2 ? 1024 : (vpt <= 4 ? 512 : 256);
+}
+
+enum EpilogueMode { kModeNorm = 0, kModeQuantToken = 1, kModeQuantBlock = 2 };
+enum QkMode { kQkLocal = 0, kQkSupplied = 1, kQkStats = 2 };
+
+struct EpilogueArgs {
+    const u32x4* partials[kMaxPartials];  // P row-major bf16 [T, H]
+    const u32x4* residual;                // bf16 [T, H]
+    const u32x4* weight;                  // bf16 [H]
+    u32x4* residual_out;                  // bf16 [T, H]
+    u32x4* norm_out;                      // bf16 [T, H] or null
+    u32x2* quant_out;                     // e4m3 [T, H] (FP8 modes)
+    float* scale_out;                     // fp32 [T] or [T, H/128] (FP8 modes)
+    int P;
+    int nvec;                             // H / 8
+    int groups;                           // H / 128 (block FP8)
+    float h;                              // H as fp32 (exact for H <= 2^24)
+    float eps;
+};
+
+struct QkArgs {
+    const uint16_t* qkv;                  // bf16 rows: q | k | v
+    int64_t row_stride;                   // elements
+    const u32x4* wq;                      // bf16 [q_size]
+    const u32x4* wk;                      // bf16 [kv_size]
+    u32x4* q_out;                         // bf16 [T, q_size]
+    u32x4* k_out;                         // bf16 [T, kv_size]
+    const float2* var_in;                 // fp32 [T, 2] (supplied mode)
+    float2* var_out;                      // fp32 [T, 2] (statistics mode)
+    int nq;                               // q_size / 8
+    int nk;                               // kv_size / 8
+    float q_size;
+    float kv_size;
+    float tp_world;
+    float eps;
+};
+
+struct LaunchShape {
+    int vpt;      // vectors per lane
+    int threads;  // workgroup size, a multiple of 64
+};
+
+// Picks vectors-per-lane and workgroup size for a row of nvec vectors.
+LaunchShape pick_shape(int nvec);
+
+hipError_t launch_epilogue(const EpilogueArgs& a, EpilogueMode mode, int64_t T, LaunchShape s,
+                           hipStream_t stream);
+hipError_t launch_qk(const QkArgs& a, QkMode mode, int64_t T, LaunchShape s, hipStream_t stream);
+hipError_t launch_e4m3_encode(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
+
+}  // namespace fusednorm

@@ -1,0 +1,353 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Bar (the tolerances stated for this path):
+  * residual_out: bit-exact (both sides perform the same fp32 additions in the
+    same order, so the stated 1-ulp allowance is not needed);
+  * norm_out, q_out, k_out: within 1 bf16 ulp;
+  * fp32 scales: relative 1e-6;
+  * e4m3 codes: bit-exact except off-by-one codes at near-ties and signed
+    zeros, which are counted and printed.
+Inputs come from the seeded generator in residual_add_rmsnorm_amd.workloads.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.compare import compare_bf16, compare_e4m3, compare_scales
+from residual_add_rmsnorm_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+EPS = 1e-6
+
+
+@pytest.fixture(scope="module")
+def fn():
+    from residual_add_rmsnorm_amd import fusednorm
+    return fusednorm
+
+
+def u16(t):
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def u8(t):
+    return t.detach().cpu().contiguous().view(torch.uint8).numpy()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+# ----------------------------------------------------------------------------- helpers
+
+MODES = {"norm": None, "quant_token": "token", "quant_block": "block"}
+
+
+def run_gpu(fn, inp, mode, want_norm=True, inplace=False):
+    parts = [p.to(DEV) for p in inp.partials]
+    res = inp.residual.to(DEV)
+    w = inp.weight.to(DEV)
+    eps = inp.workload.eps
+    rout = res if inplace else None
+    if mode == "norm":
+        norm, rout = fn.fused_add_rmsnorm(parts, res, w, eps, residual_out=rout)
+        torch.cuda.synchronize()
+        return dict(norm=norm, residual=rout)
+    norm = torch.empty_like(res) if want_norm else None
+    f = fn.fused_add_rmsnorm_quant_fp8 if mode == "quant_token" else \
+        fn.fused_add_rmsnorm_quant_fp8_block
+    q, s, rout, norm = f(parts, res, w, eps, norm_out=norm, residual_out=rout)
+    torch.cuda.synchronize()
+    return dict(norm=norm, residual=rout, codes=q, scales=s)
+
+
+def run_oracle(inp, mode, want_norm=True, rows=None):
+    parts = [wl.bits(p) for p in inp.partials]
+    res = wl.bits(inp.residual)
+    if rows is not None:
+        parts = [np.ascontiguousarray(p[rows]) for p in parts]
+        res = np.ascontiguousarray(res[rows])
+    return oracle.fused_add_rmsnorm(parts, res, wl.bits(inp.weight), inp.workload.eps,
+                                    quant=MODES[mode], want_norm=want_norm)
+
+
+def check(gpu, ref, mode, want_norm=True, rows=None, label=""):
+    def g(name, conv):
+        a = conv(gpu[name])
+        return a if rows is None else a[rows]
+    rep = [label]
+    compare_bf16(g("residual", u16), ref["residual"], max_ulp=0, what="residual_out")
+    if mode == "norm" or want_norm:
+        rep.append(str(compare_bf16(g("norm", u16), ref["norm"], what="norm_out")))
+    if mode != "norm":
+        rep.append(str(compare_e4m3(g("codes", u8), ref["codes"], ref["near_tie"])))
+        sc = gpu["scales"].cpu().numpy()
+        sc = sc if rows is None else sc[rows]
+        rel = compare_scales(sc, ref["scales"])
+        rep.append(f"scale max rel {rel:.3g}")
+    say(" | ".join(rep))
+
+
+def norm_case(T, H, P, kind="norm", sigma=0.5, outliers=0.0, seed=0):
+    w = wl.Workload(f"case", kind, T=T, H=H, P=P, sigma=sigma, outlier_frac=outliers,
+                    outlier_mult=64.0, seed=seed)
+    return wl.make_inputs(w)
+
+
+# ----------------------------------------------------------------------------- workloads
+
+@pytest.mark.parametrize("name", ["tiny", "decode"])
+def test_workload_norm_full(fn, name):
+    inp = wl.make_inputs(wl.WORKLOADS[name])
+    check(run_gpu(fn, inp, "norm"), run_oracle(inp, "norm"), "norm", label=name)
+
+
+@pytest.mark.parametrize("name", ["prefill_fp8_token", "fp8_block"])
+@pytest.mark.parametrize("want_norm", [False, True])
+def test_workload_quant_reduced(fn, name, want_norm):
+    w = wl.WORKLOADS[name]
+    inp = wl.make_inputs(w, T=384)
+    mode = w.kind
+    check(run_gpu(fn, inp, mode, want_norm), run_oracle(inp, mode, want_norm), mode, want_norm,
+          label=f"{name} T=384 norm_out={want_norm}")
+
+
+@pytest.mark.parametrize("name", ["prefill_fp8_token", "fp8_block"])
+def test_workload_quant_full_size_sampled(fn, name):
+    """Full size, as the benchmark launches it; the oracle checks 258 tokens."""
+    w = wl.WORKLOADS[name]
+    say(f"[{name}] drawing T={w.T} H={w.H} P={w.P}")
+    inp = wl.make_inputs(w)
+    gpu = run_gpu(fn, inp, w.kind, want_norm=False)
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, w.T - 1], rng.choice(w.T, 256, replace=False)]))
+    ref = run_oracle(inp, w.kind, want_norm=False, rows=rows)
+    check(gpu, ref, w.kind, want_norm=False, rows=rows, label=f"{name} full size, {len(rows)} rows")
+    # properties that hold at any size, checked on every token
+    sc = gpu["scales"].cpu().numpy()
+    assert np.all(np.isfinite(sc)) and np.all(sc > 0)
+    codes = u8(gpu["codes"]).reshape(w.T, -1, 128 if w.kind == "quant_block" else w.H)
+    top = (codes & 0x7F).max(axis=-1)
+    assert np.all(top == 0x7E), "every token / group must reach the top code"
+
+
+@pytest.mark.parametrize("name", ["qk_local", "qk_sharded"])
+def test_workload_qk_full(fn, name):
+    w = wl.WORKLOADS[name]
+    inp = wl.make_inputs(w)
+    qkv = inp.qkv.to(DEV)
+    wq, wk = inp.q_weight.to(DEV), inp.k_weight.to(DEV)
+    qkv_b = wl.bits(inp.qkv)
+    var_in = None
+    if w.tp_world > 1:
+        rows = [qkv_b] + [wl.bits(s) for s in inp.shards]
+        var_in = sum(oracle.qk_means(r, w.q_size, w.kv_size) for r in rows).astype(np.float32)
+    q, k = fn.qk_rmsnorm(qkv, w.q_size, w.kv_size, wq, wk, w.eps, w.tp_world,
+                         None if var_in is None else torch.from_numpy(var_in).to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.qk_rmsnorm(qkv_b, w.q_size, w.kv_size, wl.bits(inp.q_weight),
+                            wl.bits(inp.k_weight), w.eps, w.tp_world, var_in)
+    say(name, compare_bf16(u16(q), ref["q"], what="q_out"),
+        compare_bf16(u16(k), ref["k"], what="k_out"))
+
+
+# ----------------------------------------------------------------------------- sweeps
+
+SWEEP_NORM = [(H, P) for H in (8, 24, 64, 1000, 1024, 2048, 4096, 4104, 7168, 8192, 16384)
+              for P in (1, 3, 8, 16)] + [(7168, P) for P in (2, 4, 5, 6, 7, 9, 12)]
+
+
+@pytest.mark.parametrize("H,P", SWEEP_NORM)
+def test_sweep_norm(fn, H, P):
+    inp = norm_case(7, H, P, seed=H * 31 + P)
+    check(run_gpu(fn, inp, "norm"), run_oracle(inp, "norm"), "norm", label=f"norm H={H} P={P}")
+
+
+@pytest.mark.parametrize("H,P", [(H, P) for H in (8, 64, 1000, 4104, 7168, 8192, 16384)
+                                 for P in (1, 2, 8, 16)])
+def test_sweep_quant_token(fn, H, P):
+    inp = norm_case(7, H, P, "quant_token", outliers=0.01, seed=H * 17 + P)
+    check(run_gpu(fn, inp, "quant_token"), run_oracle(inp, "quant_token"), "quant_token",
+          label=f"token H={H} P={P}")
+
+
+@pytest.mark.parametrize("H,P", [(H, P) for H in (128, 384, 1152, 7168, 16384)
+                                 for P in (1, 2, 5, 16)])
+def test_sweep_quant_block(fn, H, P):
+    inp = norm_case(7, H, P, "quant_block", outliers=0.01, seed=H * 13 + P)
+    check(run_gpu(fn, inp, "quant_block"), run_oracle(inp, "quant_block"), "quant_block",
+          label=f"block H={H} P={P}")
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+@pytest.mark.parametrize("T", [1, 255, 4096])
+def test_token_counts(fn, mode, T):
+    inp = norm_case(T, 7168, 4, mode, seed=T)
+    check(run_gpu(fn, inp, mode), run_oracle(inp, mode), mode, label=f"{mode} T={T}")
+
+
+# ----------------------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("mode", list(MODES))
+def test_in_place_residual(fn, mode):
+    inp = norm_case(33, 4096, 3, mode, seed=77)
+    ref = run_oracle(inp, mode)
+    gpu = run_gpu(fn, inp, mode, inplace=True)
+    check(gpu, ref, mode, label=f"{mode} in-place")
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+def test_zero_and_tiny_tokens(fn, mode):
+    inp = norm_case(6, 1024, 2, mode, seed=3)
+    for p in inp.partials:
+        p[0].zero_()
+        p[1].zero_()
+    inp.residual[0].zero_()
+    inp.residual[1].zero_()
+    inp.residual[1, 5] = 1.0                                   # one nonzero channel
+    for p in inp.partials:                                     # a row of tiny magnitudes
+        p[2] = (p[2].float() * 1e-35).to(torch.bfloat16)
+    inp.residual[2] = (inp.residual[2].float() * 1e-35).to(torch.bfloat16)
+    check(run_gpu(fn, inp, mode), run_oracle(inp, mode), mode, label=f"{mode} zero/tiny rows")
+
+
+def test_empty_batch_launches_nothing(fn):
+    res = torch.zeros(0, 64, dtype=torch.bfloat16, device=DEV)
+    norm, rout = fn.fused_add_rmsnorm([res.clone()], res, torch.ones(64, dtype=torch.bfloat16,
+                                                                    device=DEV))
+    q, s, r2, _ = fn.fused_add_rmsnorm_quant_fp8([res.clone()], res,
+                                                 torch.ones(64, dtype=torch.bfloat16, device=DEV))
+    torch.cuda.synchronize()
+    assert norm.shape == (0, 64) and q.shape == (0, 64) and s.shape == (0,)
+
+
+def test_invalid_arguments_write_nothing(fn):
+    T, H = 4, 256
+    parts = [torch.randn(T, H, device=DEV).to(torch.bfloat16)]
+    res = torch.randn(T, H, device=DEV).to(torch.bfloat16)
+    w = torch.ones(H, dtype=torch.bfloat16, device=DEV)
+    norm = torch.full((T, H), 7.0, dtype=torch.bfloat16, device=DEV)
+    rout = norm.clone()
+    with pytest.raises(fn.FusedNormError) as e:
+        fn.fused_add_rmsnorm(parts, res, w, -1.0, norm_out=norm, residual_out=rout)
+    assert e.value.status == 1
+    with pytest.raises(fn.FusedNormUnsupported):
+        fn.fused_add_rmsnorm_quant_fp8_block(parts, res, w, group_size=64)
+    with pytest.raises(fn.FusedNormUnsupported):   # norm_out aliasing a partial
+        fn.fused_add_rmsnorm(parts, res, w, norm_out=parts[0], residual_out=rout)
+    with pytest.raises(ValueError):                # binding refuses a short output
+        fn.fused_add_rmsnorm(parts, res, w, norm_out=norm[:2], residual_out=rout)
+    torch.cuda.synchronize()
+    assert torch.all(norm == 7.0) and torch.all(rout == 7.0)
+
+
+def test_non_default_stream_and_determinism(fn):
+    inp = norm_case(300, 8192, 8, "quant_token", outliers=0.001, seed=9)
+    a = run_gpu(fn, inp, "quant_token")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        b = run_gpu(fn, inp, "quant_token")
+    s.synchronize()
+    for k in ("residual", "codes", "scales", "norm"):
+        assert torch.equal(a[k].view(torch.uint8) if k == "codes" else a[k],
+                           b[k].view(torch.uint8) if k == "codes" else b[k]), k
+
+
+# ----------------------------------------------------------------------------- e4m3 conversion
+
+def test_e4m3_encode_midpoints_and_neighbours(fn):
+    codes = np.arange(127, dtype=np.uint8)
+    vals = oracle.e4m3_decode(codes)
+    mid = 0.5 * (vals[:-1] + vals[1:])
+    m32 = mid.astype(np.float32)
+    assert np.array_equal(m32.astype(np.float64), mid)           # midpoints are exact in fp32
+    up = np.nextafter(m32, np.float32(np.inf))
+    dn = np.nextafter(m32, np.float32(-np.inf))
+    extra = np.array([0.0, 448.0, 448.5, 464.0, 480.0, 1e30, 2.0**-10, 2.0**-12, 1e-30,
+                      np.float32(2.0**-149)], np.float32)
+    x = np.concatenate([m32, up, dn, vals.astype(np.float32), extra])
+    x = np.concatenate([x, -x]).astype(np.float32)
+    rng = np.random.default_rng(0)
+    rnd = (rng.standard_normal(100003) * np.exp2(rng.integers(-12, 9, 100003))).astype(np.float32)
+    x = np.concatenate([x, np.clip(rnd, -1e4, 1e4)]).astype(np.float32)
+    got = u8(fn.e4m3_encode(torch.from_numpy(x).to(DEV)))
+    want = oracle.e4m3_encode(x.astype(np.float64))
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(float(x[i]), hex(got[i]), hex(want[i])) for i in bad[:8]]
+
+
+@pytest.mark.parametrize("n", [1, 7, 8, 9, 1000, 4099])
+def test_e4m3_encode_ragged_lengths(fn, n):
+    x = np.linspace(-500, 500, n).astype(np.float32)
+    buf = torch.full((n + 64,), 0xAB, dtype=torch.uint8, device=DEV)
+    out = buf[:n]
+    fn.e4m3_encode(torch.from_numpy(x).to(DEV), out=out)
+    torch.cuda.synchronize()
+    assert np.array_equal(u8(out), oracle.e4m3_encode(x.astype(np.float64)))
+    assert torch.all(buf[n:] == 0xAB)                            # nothing past the end
+
+
+# ----------------------------------------------------------------------------- QK edge cases
+
+@pytest.mark.parametrize("q,k,stride", [(8, 8, 24), (48, 16, 96), (48, 16, 200),
+                                        (1024, 128, 1280), (6144, 1024, 8192),
+                                        (12288, 2048, 16384)])
+@pytest.mark.parametrize("supplied", [False, True])
+def test_qk_shapes_strides_and_poisoned_v(fn, q, k, stride, supplied):
+    T = 37
+    g = torch.Generator().manual_seed(q + k + stride)
+    base = torch.randn(T, stride, generator=g).to(torch.bfloat16)
+    base[:, q + k:] = float("nan")                                 # v and padding: never read
+    wq = (1 + 0.1 * torch.randn(q, generator=g)).to(torch.bfloat16)
+    wk = (1 + 0.1 * torch.randn(k, generator=g)).to(torch.bfloat16)
+    b = wl.bits(base)
+    var_in, tp = None, 1
+    if supplied:
+        var_in = (oracle.qk_means(b, q, k) * 3).astype(np.float32)   # as if 3 equal shards
+        tp = 3
+    qo, ko = fn.qk_rmsnorm(base.to(DEV), q, k, wq.to(DEV), wk.to(DEV), EPS, tp,
+                           None if var_in is None else torch.from_numpy(var_in).to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.qk_rmsnorm(b, q, k, wl.bits(wq), wl.bits(wk), EPS, tp, var_in)
+    compare_bf16(u16(qo), ref["q"], what="q_out")
+    compare_bf16(u16(ko), ref["k"], what="k_out")
+
+
+def test_qk_strided_view_of_a_wider_tensor(fn):
+    T, q, k = 64, 6144, 1024
+    big = torch.randn(T, 8192 + 512, dtype=torch.float32).to(torch.bfloat16)
+    view = big[:, 256:256 + 8192]                                  # offset 512 B: aligned
+    wq = torch.ones(q, dtype=torch.bfloat16)
+    wk = torch.ones(k, dtype=torch.bfloat16)
+    qo, ko = fn.qk_rmsnorm(big.to(DEV)[:, 256:256 + 8192], q, k, wq.to(DEV), wk.to(DEV))
+    torch.cuda.synchronize()
+    vb = np.ascontiguousarray(wl.bits(big)[:, 256:256 + 8192])
+    ref = oracle.qk_rmsnorm(vb, q, k, wl.bits(wq), wl.bits(wk), EPS)
+    compare_bf16(u16(qo), ref["q"], what="q_out")
+    compare_bf16(u16(ko), ref["k"], what="k_out")
+    assert qo.is_contiguous() and ko.is_contiguous() and view.shape == (T, 8192)
+
+
+def test_qk_local_means_stage(fn):
+    w = wl.WORKLOADS["qk_local"]
+    inp = wl.make_inputs(w, T=512)
+    var = fn.qk_rmsnorm_var(inp.qkv.to(DEV), w.q_size, w.kv_size)
+    torch.cuda.synchronize()
+    ref = oracle.qk_means(wl.bits(inp.qkv), w.q_size, w.kv_size)
+    rel = compare_scales(var.cpu().numpy(), ref, rtol=1e-6, what="local means")
+    say(f"qk local means: max rel {rel:.3g}")
+
+
+def test_qk_empty_and_invalid(fn):
+    qkv = torch.zeros(0, 96, dtype=torch.bfloat16, device=DEV)
+    w = torch.ones(48, dtype=torch.bfloat16, device=DEV)
+    qo, ko = fn.qk_rmsnorm(qkv, 48, 16, w, w[:16])
+    assert qo.shape == (0, 48)
+    qkv = torch.zeros(4, 96, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(fn.FusedNormError):
+        fn.qk_rmsnorm(qkv, 48, 16, w, w[:16].contiguous(), tp_world=4)
