@@ -90,8 +90,8 @@ class Part:
                 self.var_in = sum(fn.qk_rmsnorm_var(s, w.q_size, w.kv_size) for s in shards)
                 del shards
             self.call = lambda: fn.qk_rmsnorm(self.qkv, w.q_size, w.kv_size, self.wq, self.wk,
-                                              w.eps, w.tp_world, self.var_in, self.q_out,
-                                              self.k_out)
+                                              w.eps, tp_world=w.tp_world, var_in=self.var_in,
+                                              q_out=self.q_out, k_out=self.k_out)
         else:
             self.parts = [p.to(dev) for p in self.cpu.partials]
             self.res = self.cpu.residual.to(dev)
@@ -105,8 +105,9 @@ class Part:
                 self.scale = torch.empty(w.T, w.H // w.group_size, dtype=torch.float32,
                                          device=dev)
                 f = fn.fused_add_rmsnorm_quant_fp8_block
-            self.call = lambda: f(self.parts, self.res, self.weight, w.eps, None, self.res_out,
-                                  self.quant, self.scale)
+            self.call = lambda: f(self.parts, self.res, self.weight, w.eps, norm_out=None,
+                                  residual_out=self.res_out, quant_out=self.quant,
+                                  scale_out=self.scale)
         self.bytes = w.algorithmic_bytes()
         log(f"[bench] {name}: {w.description}; {self.bytes / 1e6:.1f} MB per launch "
             f"(inputs drawn in {time.perf_counter() - t0:.1f} s)")
