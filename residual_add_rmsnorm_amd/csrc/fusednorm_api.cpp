@@ -164,14 +164,19 @@ int fused_common(const void* const* partials, int P, const void* residual_in, co
     a.scale_out = scale_out;
     a.P = P;
     a.nvec = (int)(H / 8);
+    a.row_bytes = (uint32_t)(H * 2);
     a.groups = (int)(H / FUSEDNORM_FP8_GROUP);
     a.h = (float)H;
     a.eps = eps;
     const fusednorm::EpilogueMode mode = quant == Quant::None    ? fusednorm::kModeNorm
                                          : quant == Quant::Token ? fusednorm::kModeQuantToken
                                                                  : fusednorm::kModeQuantBlock;
-    const fusednorm::LaunchShape shape = fusednorm::pick_shape(a.nvec);
     (void)hipGetLastError();  // start from a clean error state
+    int cus = 0;
+    if (hipError_t e = fusednorm::device_cus(&cus)) return hip_status(e, "device query");
+    const fusednorm::LaunchShape shape = fusednorm::pick_epilogue_shape(a.nvec, P, T, cus);
+    if (shape.vpt == 0)
+        return fail(FUSEDNORM_ERR_UNSUPPORTED, "no launch shape covers H = %lld", (long long)H);
     return hip_status(fusednorm::launch_epilogue(a, mode, T, shape, (hipStream_t)stream),
                       "kernel launch");
 }
@@ -252,8 +257,12 @@ int qk_common(const void* qkv, int64_t T, int64_t row_stride, int64_t q_size, in
     a.tp_world = (float)tp_world;
     a.eps = eps;
     if (!stats) mode = var_in ? fusednorm::kQkSupplied : fusednorm::kQkLocal;
-    const fusednorm::LaunchShape shape = fusednorm::pick_shape(a.nq + a.nk);
     (void)hipGetLastError();
+    int cus = 0;
+    if (hipError_t e = fusednorm::device_cus(&cus)) return hip_status(e, "device query");
+    const fusednorm::LaunchShape shape = fusednorm::pick_qk_shape(a.nq + a.nk, T, cus);
+    if (shape.vpt == 0)
+        return fail(FUSEDNORM_ERR_UNSUPPORTED, "no launch shape covers q_size + kv_size");
     return hip_status(fusednorm::launch_qk(a, mode, T, shape, (hipStream_t)stream), "kernel launch");
 }
 

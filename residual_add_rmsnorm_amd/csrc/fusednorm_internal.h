@@ -14,12 +14,19 @@ constexpr int kWave = 64;
 constexpr int kMaxWaves = 16;   // 1024 threads per workgroup
 constexpr int kMaxPartials = 16;
 constexpr int kMaxVpt = 8;      // 16-byte vectors per lane per token
+// The fused epilogue keeps CH*VPT prefetched 16-byte vectors per lane (CH =
+// partial buffers loaded together); beyond this the kernel would spill.
+constexpr int kMaxLoadsPerLane = 16;
 
-// Largest workgroup each vectors-per-lane variant is compiled for: more
-// vectors per lane hold more loads in flight and need more VGPRs, so fewer
-// waves may share a CU.
+// Largest workgroup each variant is compiled for. More vectors per lane (and,
+// for the fused epilogue, more partials loaded together) hold more loads in
+// flight and need more VGPRs: a 1024-thread workgroup leaves 128 VGPRs per
+// lane, 512 threads 256, 256 threads 512.
 constexpr __host__ __device__ int max_threads_for(int vpt) {
     return vpt <= 2 ? 1024 : (vpt <= 4 ? 512 : 256);
+}
+constexpr __host__ __device__ int max_threads_for(int vpt, int ch) {
+    return (vpt <= 2 && vpt * ch <= 8) ? 1024 : (vpt <= 4 ? 512 : 256);
 }
 
 enum EpilogueMode { kModeNorm = 0, kModeQuantToken = 1, kModeQuantBlock = 2 };
@@ -35,6 +42,7 @@ struct EpilogueArgs {
     float* scale_out;                     // fp32 [T] or [T, H/128] (FP8 modes)
     int P;
     int nvec;                             // H / 8
+    uint32_t row_bytes;                   // H * 2
     int groups;                           // H / 128 (block FP8)
     float h;                              // H as fp32 (exact for H <= 2^24)
     float eps;
@@ -58,12 +66,20 @@ struct QkArgs {
 };
 
 struct LaunchShape {
-    int vpt;      // vectors per lane
+    int vpt;      // 16-byte vectors per lane
     int threads;  // workgroup size, a multiple of 64
+    int ch;       // fused epilogue: partial buffers loaded together (2, 4 or 8)
 };
 
-// Picks vectors-per-lane and workgroup size for a row of nvec vectors.
-LaunchShape pick_shape(int nvec);
+// Launch shape of the fused epilogue for T rows of nvec 16-byte vectors and P
+// partial buffers, and of the QK norm for T rows of nvec vectors, on a device
+// with `cus` compute units. The shape decides only speed; every shape
+// computes the same result. A shape with vpt == 0 means none fits.
+LaunchShape pick_epilogue_shape(int nvec, int P, int64_t T, int cus);
+LaunchShape pick_qk_shape(int nvec, int64_t T, int cus);
+
+// Compute units of the current device (cached per device).
+hipError_t device_cus(int* cus);
 
 hipError_t launch_epilogue(const EpilogueArgs& a, EpilogueMode mode, int64_t T, LaunchShape s,
                            hipStream_t stream);

@@ -8,12 +8,16 @@
 // and the vLLM minimax_rms_norm/rms_norm_tp page (_minimax_qk_var_kernel,
 // _minimax_rms_apply_kernel). How it is computed is designed for CDNA4:
 //
-//   * one workgroup per token; the row is cut into 16-byte vectors (8 bf16)
-//     and vector i belongs to lane i mod blockDim, slot i / blockDim, so every
-//     wave-wide load or store covers 1 KiB of consecutive bytes;
-//   * every load a lane needs for its token (P partials, residual, weight) is
-//     issued before the first add: a wave keeps (P+2)*VPT 16-byte requests in
-//     flight to HBM;
+//   * persistent workgroups: workgroup b handles tokens b, b + G, b + 2G, ...
+//     (G = at most two resident workgroups per CU), and issues the next
+//     token's loads as soon as the current token's sum is formed, so HBM
+//     requests stay in flight while a token is reduced, normalised and stored;
+//     the weight vector is loaded once per workgroup;
+//   * a token's row is cut into 16-byte vectors (8 bf16); vector i belongs to
+//     lane i mod blockDim, slot i / blockDim, so every wave-wide access covers
+//     1 KiB of consecutive bytes, read and written through per-row buffer
+//     resources with the non-temporal policy (lanes past the row end read
+//     zeros and their stores are dropped by the hardware range check);
 //   * the fp32 row stays in VGPRs between the reduction and the normalisation;
 //     sums and maxima are reduced inside a wave with DPP row permutes plus two
 //     cross-row lane shuffles, then across the token's waves through LDS;
@@ -23,6 +27,9 @@
 //     packed conversions v_cvt_pk_bf16_f32 and v_cvt_pk_fp8_f32.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <mutex>
+#include <vector>
 
 #include "fusednorm_internal.h"
 
@@ -78,12 +85,33 @@ __device__ __forceinline__ u32x2 pack_e4m3x8(const float (&r)[8]) {
 
 // ---------------------------------------------------------------- global memory
 
-// Read-once streams (partials, residual, qkv) and write-once outputs use
-// non-temporal accesses so they do not displace the weight vector, which
-// every token of the launch re-reads.
-__device__ __forceinline__ u32x4 load_stream(const u32x4* p) { return __builtin_nontemporal_load(p); }
-__device__ __forceinline__ void store_stream(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
-__device__ __forceinline__ void store_stream(u32x2* p, u32x2 v) { __builtin_nontemporal_store(v, p); }
+// Token rows are read and written through buffer resources: a resource covers
+// one row of one stream (wave-uniform, held in SGPRs) and each lane adds its
+// byte offset, the same offset for every stream of the row. The hardware range
+// check of the resource makes a lane past the end of the row read zeros and
+// drop its stores, so a row access can never touch memory outside that row.
+// Read-once inputs and write-once outputs carry the non-temporal policy bit so
+// they do not displace the weights, which every token re-reads.
+constexpr int kBufferFormat = 0x00020000;  // buffer descriptor word 3 for gfx9-family raw access
+constexpr int kPolicyStream = 2;           // cache policy: nt (sc0 = bit 0, nt = bit 1, sc1 = bit 4)
+
+struct Row {
+    __amdgpu_buffer_rsrc_t rsrc;
+};
+
+__device__ __forceinline__ Row make_row(const void* base, uint32_t bytes) {
+    return Row{__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                                 kBufferFormat)};
+}
+__device__ __forceinline__ u32x4 load16(Row r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r.rsrc, off, 0, kPolicyStream);
+}
+__device__ __forceinline__ void store16(Row r, uint32_t off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r.rsrc, off, 0, kPolicyStream);
+}
+__device__ __forceinline__ void store8(Row r, uint32_t off, u32x2 v) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, r.rsrc, off, 0, kPolicyStream);
+}
 
 __device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 
@@ -119,9 +147,12 @@ __device__ __forceinline__ float wave_reduce(float v, Op op) {
 
 // Workgroup reduction of a sum s and, when TWO, a second value m combined with
 // Op2. Every thread receives the same results; waves are combined in order.
+// A workgroup that loops over tokens alternates between two LDS buffers
+// (buf = token parity): a wave can only come back to a buffer after the next
+// token's barrier, which every wave reaches after reading this one.
 template <bool TWO, class Op2>
-__device__ __forceinline__ void block_reduce(float& s, float& m, Op2 op2) {
-    __shared__ float red[2][kMaxWaves];
+__device__ __forceinline__ void block_reduce(float& s, float& m, Op2 op2, int buf) {
+    __shared__ float red[2][2][kMaxWaves];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int nwaves = blockDim.x / kWave;
@@ -129,15 +160,15 @@ __device__ __forceinline__ void block_reduce(float& s, float& m, Op2 op2) {
     if (TWO) m = wave_reduce(m, op2);
     if (nwaves == 1) return;
     if (lane == 0) {
-        red[0][wave] = s;
-        if (TWO) red[1][wave] = m;
+        red[buf][0][wave] = s;
+        if (TWO) red[buf][1][wave] = m;
     }
     __syncthreads();
-    s = red[0][0];
-    if (TWO) m = red[1][0];
+    s = red[buf][0][0];
+    if (TWO) m = red[buf][1][0];
     for (int w = 1; w < nwaves; ++w) {
-        s += red[0][w];
-        if (TWO) m = op2(m, red[1][w]);
+        s += red[buf][0][w];
+        if (TWO) m = op2(m, red[buf][1][w]);
     }
 }
 
@@ -160,14 +191,15 @@ __device__ __forceinline__ float tree_sum(float (&v)[N]) {
 // Adds partial buffers P0 .. P0+N-1 to the fp32 accumulators, in partial
 // order. All N*VPT loads are issued before the first add.
 template <int N, int P0, int VPT>
-__device__ __forceinline__ void add_partials(const EpilogueArgs& a, int64_t row, int tid, int nthr,
-                                             const bool (&valid)[VPT], float (&x)[VPT][8]) {
+__device__ __forceinline__ void add_partials(const EpilogueArgs& a, int64_t row,
+                                             const uint32_t (&off)[VPT], float (&x)[VPT][8]) {
     u32x4 v[N][VPT];
 #pragma unroll
-    for (int k = 0; k < N; ++k)
+    for (int k = 0; k < N; ++k) {
+        const Row r = make_row(a.partials[P0 + k] + row, a.row_bytes);
 #pragma unroll
-        for (int s = 0; s < VPT; ++s)
-            v[k][s] = valid[s] ? load_stream(a.partials[P0 + k] + row + s * nthr + tid) : zero4();
+        for (int s = 0; s < VPT; ++s) v[k][s] = load16(r, off[s]);
+    }
 #pragma unroll
     for (int k = 0; k < N; ++k)
 #pragma unroll
@@ -181,14 +213,13 @@ __device__ __forceinline__ void add_partials(const EpilogueArgs& a, int64_t row,
 
 // Adds exactly n partials (1 <= n <= N) starting at partial P0.
 template <int N, int P0, int VPT>
-__device__ __forceinline__ void add_partials_upto(int n, const EpilogueArgs& a, int64_t row, int tid,
-                                                  int nthr, const bool (&valid)[VPT],
-                                                  float (&x)[VPT][8]) {
+__device__ __forceinline__ void add_partials_upto(int n, const EpilogueArgs& a, int64_t row,
+                                                  const uint32_t (&off)[VPT], float (&x)[VPT][8]) {
     if constexpr (N == 1) {
-        add_partials<1, P0>(a, row, tid, nthr, valid, x);
+        add_partials<1, P0>(a, row, off, x);
     } else {
-        if (n == N) add_partials<N, P0>(a, row, tid, nthr, valid, x);
-        else add_partials_upto<N - 1, P0>(n, a, row, tid, nthr, valid, x);
+        if (n == N) add_partials<N, P0>(a, row, off, x);
+        else add_partials_upto<N - 1, P0>(n, a, row, off, x);
     }
 }
 
@@ -196,19 +227,18 @@ __device__ __forceinline__ void add_partials_upto(int n, const EpilogueArgs& a, 
 // flight together, so a kernel compiled for chunk CH holds CH*VPT vectors of
 // loads in registers.
 template <int CH, int P0, int VPT>
-__device__ __forceinline__ void add_all_partials(int P, const EpilogueArgs& a, int64_t row, int tid,
-                                                 int nthr, const bool (&valid)[VPT],
-                                                 float (&x)[VPT][8]) {
+__device__ __forceinline__ void add_all_partials(int P, const EpilogueArgs& a, int64_t row,
+                                                 const uint32_t (&off)[VPT], float (&x)[VPT][8]) {
     if constexpr (P0 < kMaxPartials) {
         if (P > P0) {
             const int n = P - P0;
             if constexpr (CH == 1) {
-                add_partials<1, P0>(a, row, tid, nthr, valid, x);
+                add_partials<1, P0>(a, row, off, x);
             } else {
-                if (n >= CH) add_partials<CH, P0>(a, row, tid, nthr, valid, x);
-                else add_partials_upto<CH - 1, P0>(n, a, row, tid, nthr, valid, x);
+                if (n >= CH) add_partials<CH, P0>(a, row, off, x);
+                else add_partials_upto<CH - 1, P0>(n, a, row, off, x);
             }
-            add_all_partials<CH, P0 + CH>(P, a, row, tid, nthr, valid, x);
+            add_all_partials<CH, P0 + CH>(P, a, row, off, x);
         }
     }
 }
@@ -234,87 +264,148 @@ __device__ __forceinline__ QuantScale quant_scale(float xw_max) {
     return q;
 }
 
-template <int VPT, int MODE, int CH>
-__global__ void __launch_bounds__(max_threads_for(VPT)) fused_epilogue_kernel(EpilogueArgs a) {
-    const int tid = threadIdx.x;
-    const int nthr = blockDim.x;
-    const int64_t t = blockIdx.x;
-    const int64_t row = t * a.nvec;  // start of the token's row, in 16-byte vectors
+// The loads of one token that are issued ahead of its arithmetic: the first
+// chunk of up to CH partial buffers and the residual.
+template <int VPT, int CH>
+struct TokenLoads {
+    u32x4 part[CH][VPT];
+    u32x4 res[VPT];
+};
 
-    bool valid[VPT];
-    u32x4 res[VPT], wv[VPT];
+template <int VPT, int CH>
+__device__ __forceinline__ void issue_token_loads(const EpilogueArgs& a, int n0, int64_t row,
+                                                  const uint32_t (&off)[VPT],
+                                                  TokenLoads<VPT, CH>& L) {
 #pragma unroll
-    for (int s = 0; s < VPT; ++s) {
-        const int i = s * nthr + tid;
-        valid[s] = i < a.nvec;
-        res[s] = valid[s] ? load_stream(a.residual + row + i) : zero4();
-        wv[s] = valid[s] ? a.weight[i] : zero4();
-    }
+    for (int k = 0; k < CH; ++k)
+        if (k < n0) {
+            const Row r = make_row(a.partials[k] + row, a.row_bytes);
+#pragma unroll
+            for (int s = 0; s < VPT; ++s) L.part[k][s] = load16(r, off[s]);
+        }
+    const Row r = make_row(a.residual + row, a.row_bytes);
+#pragma unroll
+    for (int s = 0; s < VPT; ++s) L.res[s] = load16(r, off[s]);
+}
 
-    // x = (((0 + p_0) + p_1) + ... + p_{P-1}) + residual, in fp32.
-    float x[VPT][8];
+// x = (((0 + p_0) + p_1) + ... + p_{P-1}) + residual, in fp32: the first chunk
+// from the loads already in flight, any further partials (P > CH) loaded here
+// two at a time, which keeps their registers off the prefetch's budget.
+template <int VPT, int CH>
+__device__ __forceinline__ void sum_token(const EpilogueArgs& a, int n0, int64_t row,
+                                          const uint32_t (&off)[VPT],
+                                          const TokenLoads<VPT, CH>& L, float (&x)[VPT][8]) {
 #pragma unroll
     for (int s = 0; s < VPT; ++s)
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[s][e] = 0.0f;
-    add_all_partials<CH, 0>(a.P, a, row, tid, nthr, valid, x);
+#pragma unroll
+    for (int k = 0; k < CH; ++k)
+        if (k < n0) {
+#pragma unroll
+            for (int s = 0; s < VPT; ++s) {
+                float f[8];
+                unpack8(L.part[k][s], f);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[s][e] += f[e];
+            }
+        }
+    add_all_partials<2, CH>(a.P, a, row, off, x);
 #pragma unroll
     for (int s = 0; s < VPT; ++s) {
         float r[8];
-        unpack8(res[s], r);
+        unpack8(L.res[s], r);
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[s][e] += r[e];
     }
+}
 
-    // Token statistics: sum of x^2 and, for per-token FP8, max |x*w|.
-    float part[VPT];
-    float xw_max = 0.0f;
-#pragma unroll
-    for (int s = 0; s < VPT; ++s) {
-        part[s] = sumsq8(x[s]);
-        if (MODE == kModeQuantToken) {
-            float w[8];
-            unpack8(wv[s], w);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) xw_max = fmaxf(xw_max, fabsf(x[s][e] * w[e]));
-        }
-    }
-    float ss = tree_sum(part);
-    block_reduce<MODE == kModeQuantToken>(ss, xw_max, Max{});
-    const float inv = rsqrtf(ss / a.h + a.eps);
+// One workgroup handles tokens blockIdx.x, blockIdx.x + gridDim.x, ... (the
+// grid holds as many workgroups as fit on the GPU at once). The next token's
+// loads are issued as soon as the current token's sum is formed, so they are
+// in flight while the current token is reduced, normalised and stored.
+template <int VPT, int MODE, int CH>
+__global__ void __launch_bounds__(max_threads_for(VPT, CH))
+fused_epilogue_kernel(EpilogueArgs a, int64_t T) {
+    const int tid = threadIdx.x;
+    const int nthr = blockDim.x;
+    const int n0 = a.P < CH ? a.P : CH;
 
-    // y / (amax_y / 448) = 448 * x*w / max|x*w|: the rsqrt cancels, so the
-    // codes come straight from x*w.
-    QuantScale token_q{1.0f, 0.0f};
-    if (MODE == kModeQuantToken) {
-        token_q = quant_scale(xw_max);
-        if (tid == 0) a.scale_out[t] = (xw_max * inv) / 448.0f;
-    }
-
+    bool valid[VPT];
+    uint32_t off[VPT];  // byte offset of the lane's vector in slot s, within a bf16 row
+    u32x4 wv[VPT];      // the weight: loaded once, used for every token of the workgroup
 #pragma unroll
     for (int s = 0; s < VPT; ++s) {
         const int i = s * nthr + tid;
-        float w[8], xw[8];
-        unpack8(wv[s], w);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) xw[e] = x[s][e] * w[e];
+        valid[s] = i < a.nvec;
+        off[s] = (uint32_t)i * 16u;
+        wv[s] = valid[s] ? a.weight[i] : zero4();
+    }
 
-        QuantScale q = token_q;
-        float group_max = 0.0f;
-        if (MODE == kModeQuantBlock) {
-            // every lane takes part: the 16 lanes of this DPP row hold one group
+    int64_t t = blockIdx.x;  // the host launches at most T workgroups
+    TokenLoads<VPT, CH> L;
+    issue_token_loads(a, n0, t * a.nvec, off, L);
+    for (int parity = 0;; parity ^= 1) {
+        const int64_t row = t * a.nvec;  // start of the token's row, in 16-byte vectors
+        float x[VPT][8];
+        sum_token(a, n0, row, off, L, x);
+        const int64_t t_next = t + gridDim.x;
+        const bool more = t_next < T;
+        if (more) issue_token_loads(a, n0, t_next * a.nvec, off, L);
+
+        // Token statistics: sum of x^2 and, for per-token FP8, max |x*w|.
+        float part[VPT];
+        float xw_max = 0.0f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) group_max = fmaxf(group_max, fabsf(xw[e]));
-            group_max = row16_reduce(group_max, Max{});
-            q = quant_scale(group_max);
+        for (int s = 0; s < VPT; ++s) {
+            part[s] = sumsq8(x[s]);
+            if (MODE == kModeQuantToken) {
+                float w[8];
+                unpack8(wv[s], w);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) xw_max = fmaxf(xw_max, fabsf(x[s][e] * w[e]));
+            }
         }
-        if (valid[s]) {
-            store_stream(a.residual_out + row + i, pack_bf16x8(x[s]));
+        float ss = tree_sum(part);
+        block_reduce<MODE == kModeQuantToken>(ss, xw_max, Max{}, parity);
+        const float inv = rsqrtf(ss / a.h + a.eps);
+
+        // y / (amax_y / 448) = 448 * x*w / max|x*w|: the rsqrt cancels, so the
+        // codes come straight from x*w.
+        QuantScale token_q{1.0f, 0.0f};
+        if (MODE == kModeQuantToken) {
+            token_q = quant_scale(xw_max);
+            if (tid == 0) a.scale_out[t] = (xw_max * inv) / 448.0f;
+        }
+
+        const Row out_res = make_row(a.residual_out + row, a.row_bytes);
+        const Row out_norm = a.norm_out ? make_row(a.norm_out + row, a.row_bytes) : out_res;
+        const Row out_q = MODE != kModeNorm ? make_row(a.quant_out + row, a.row_bytes / 2u) : out_res;
+#pragma unroll
+        for (int s = 0; s < VPT; ++s) {
+            const int i = s * nthr + tid;
+            float w[8], xw[8];
+            unpack8(wv[s], w);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xw[e] = x[s][e] * w[e];
+
+            QuantScale q = token_q;
+            float group_max = 0.0f;
+            if (MODE == kModeQuantBlock) {
+                // every lane takes part: the 16 lanes of this DPP row hold one group
+#pragma unroll
+                for (int e = 0; e < 8; ++e) group_max = fmaxf(group_max, fabsf(xw[e]));
+                group_max = row16_reduce(group_max, Max{});
+                q = quant_scale(group_max);
+            }
+            // lanes past the end of the row (valid[s] false) are dropped by the
+            // resources' range check
+            store16(out_res, off[s], pack_bf16x8(x[s]));
             if (a.norm_out) {
                 float y[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) y[e] = (x[s][e] * inv) * w[e];
-                store_stream(a.norm_out + row + i, pack_bf16x8(y));
+                store16(out_norm, off[s], pack_bf16x8(y));
             }
             if (MODE != kModeNorm) {
                 float r[8];
@@ -322,77 +413,108 @@ __global__ void __launch_bounds__(max_threads_for(VPT)) fused_epilogue_kernel(Ep
                 for (int e = 0; e < 8; ++e) r[e] = (xw[e] * q.pre) * q.qmul;
                 u32x2 codes = pack_e4m3x8(r);
                 if (q.qmul == 0.0f) codes = u32x2{0u, 0u};  // all-zero token or group: +0 codes
-                store_stream(a.quant_out + row + i, codes);
-                if (MODE == kModeQuantBlock && (tid & 15) == 0)
+                store8(out_q, off[s] / 2u, codes);
+                if (MODE == kModeQuantBlock && valid[s] && (tid & 15) == 0)
                     a.scale_out[t * a.groups + i / 16] = (group_max * inv) / 448.0f;
             }
         }
+        if (!more) break;
+        t = t_next;
     }
 }
 
 // ---------------------------------------------------------------- QK RMSNorm
 
+// One workgroup per token at a time, looping over tokens blockIdx.x,
+// blockIdx.x + gridDim.x, ... like the fused epilogue; the next token's row is
+// loaded while the current one is reduced and written.
 template <int VPT, int MODE>
-__global__ void __launch_bounds__(max_threads_for(VPT)) qk_norm_kernel(QkArgs a) {
+__global__ void __launch_bounds__(max_threads_for(VPT)) qk_norm_kernel(QkArgs a, int64_t T) {
     const int tid = threadIdx.x;
     const int nthr = blockDim.x;
-    const int64_t t = blockIdx.x;
     const int nv = a.nq + a.nk;
-    // q then k lie back to back at the start of the row: one span of nv vectors.
-    const u32x4* src = reinterpret_cast<const u32x4*>(a.qkv + t * a.row_stride);
 
-    bool valid[VPT];
-    u32x4 raw[VPT];
+    // q then k lie back to back at the start of each row: one span of nv vectors.
+    bool valid[VPT], is_q[VPT];
+    uint32_t off[VPT];  // byte offset of the lane's vector in slot s, within a row
+    u32x4 wv[VPT];      // the q or k weight of each vector, loaded once
 #pragma unroll
     for (int s = 0; s < VPT; ++s) {
         const int i = s * nthr + tid;
         valid[s] = i < nv;
-        raw[s] = valid[s] ? load_stream(src + i) : zero4();
+        is_q[s] = i < a.nq;
+        off[s] = (uint32_t)i * 16u;
+        wv[s] = !valid[s] ? zero4() : is_q[s] ? a.wq[i] : a.wk[i - a.nq];
     }
 
-    float var_q, var_k;
-    if (MODE == kQkSupplied) {
-        const float2 v = a.var_in[t];
-        var_q = v.x;
-        var_k = v.y;
-    } else {
-        float sq[VPT], sk[VPT];
+    int64_t t = blockIdx.x;  // the host launches at most T workgroups
+    u32x4 next[VPT];
+    float2 next_var = make_float2(0.0f, 0.0f);
+    const uint32_t qk_bytes = (uint32_t)nv * 16u;  // q and k; v is never read
+    {
+        const Row src = make_row(a.qkv + t * a.row_stride, qk_bytes);
 #pragma unroll
-        for (int s = 0; s < VPT; ++s) {
-            const int i = s * nthr + tid;
-            float f[8];
-            unpack8(raw[s], f);
-            const float v = sumsq8(f);
-            sq[s] = i < a.nq ? v : 0.0f;
-            sk[s] = i < a.nq ? 0.0f : v;
+        for (int s = 0; s < VPT; ++s) next[s] = load16(src, off[s]);
+    }
+    if (MODE == kQkSupplied) next_var = a.var_in[t];
+
+    for (int parity = 0;; parity ^= 1) {
+        u32x4 raw[VPT];
+#pragma unroll
+        for (int s = 0; s < VPT; ++s) raw[s] = next[s];  // lanes past the row hold zeros
+        const float2 var_in = next_var;
+        const int64_t t_next = t + gridDim.x;
+        const bool more = t_next < T;
+        if (more) {
+            const Row src = make_row(a.qkv + t_next * a.row_stride, qk_bytes);
+#pragma unroll
+            for (int s = 0; s < VPT; ++s) next[s] = load16(src, off[s]);
+            if (MODE == kQkSupplied) next_var = a.var_in[t_next];
         }
-        float tq = tree_sum(sq), tk = tree_sum(sk);
-        block_reduce<true>(tq, tk, Sum{});
-        var_q = tq / a.q_size;
-        var_k = tk / a.kv_size;
+
+        float var_q, var_k;
+        if (MODE == kQkSupplied) {
+            var_q = var_in.x;
+            var_k = var_in.y;
+        } else {
+            float sq[VPT], sk[VPT];
+#pragma unroll
+            for (int s = 0; s < VPT; ++s) {
+                float f[8];
+                unpack8(raw[s], f);
+                const float v = sumsq8(f);
+                sq[s] = is_q[s] ? v : 0.0f;
+                sk[s] = is_q[s] ? 0.0f : v;
+            }
+            float tq = tree_sum(sq), tk = tree_sum(sk);
+            block_reduce<true>(tq, tk, Sum{}, parity);
+            var_q = tq / a.q_size;
+            var_k = tk / a.kv_size;
+        }
         if (MODE == kQkStats) {
             if (tid == 0) a.var_out[t] = make_float2(var_q, var_k);
-            return;
-        }
-    }
-    const float inv_q = rsqrtf(var_q / a.tp_world + a.eps);
-    const float inv_k = rsqrtf(var_k / a.tp_world + a.eps);
-
+        } else {
+            const float inv_q = rsqrtf(var_q / a.tp_world + a.eps);
+            const float inv_k = rsqrtf(var_k / a.tp_world + a.eps);
+            const Row out_q = make_row(a.q_out + t * a.nq, (uint32_t)a.nq * 16u);
+            const Row out_k = make_row(a.k_out + t * a.nk, (uint32_t)a.nk * 16u);
 #pragma unroll
-    for (int s = 0; s < VPT; ++s) {
-        const int i = s * nthr + tid;
-        if (valid[s]) {
-            const bool is_q = i < a.nq;
-            const u32x4 wraw = is_q ? a.wq[i] : a.wk[i - a.nq];
-            const float inv = is_q ? inv_q : inv_k;
-            float f[8], w[8], y[8];
-            unpack8(raw[s], f);
-            unpack8(wraw, w);
+            for (int s = 0; s < VPT; ++s) {
+                const float inv = is_q[s] ? inv_q : inv_k;
+                float f[8], w[8], y[8];
+                unpack8(raw[s], f);
+                unpack8(wv[s], w);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) y[e] = (f[e] * inv) * w[e];
-            u32x4* dst = is_q ? a.q_out + t * a.nq + i : a.k_out + t * a.nk + (i - a.nq);
-            store_stream(dst, pack_bf16x8(y));
+                for (int e = 0; e < 8; ++e) y[e] = (f[e] * inv) * w[e];
+                // a k vector's offset within q_out is past its end, and a q
+                // vector's offset within k_out wraps past k_out's end: the range
+                // check drops the store that does not apply
+                store16(out_q, off[s], pack_bf16x8(y));
+                store16(out_k, off[s] - (uint32_t)a.nq * 16u, pack_bf16x8(y));
+            }
         }
+        if (!more) break;
+        t = t_next;
     }
 }
 
@@ -415,58 +537,123 @@ __global__ void __launch_bounds__(256) e4m3_encode_kernel(const float* in, uint8
 
 // ---------------------------------------------------------------- dispatch
 
+// Compute units of the current device, and workgroups of `kernel` that fit
+// on one CU at once; cached per device, kernel and workgroup size.
+struct Residency {
+    int cus;
+    int per_cu;
+};
+
+hipError_t residency(const void* kernel, int threads, Residency* out) {
+    struct Entry {
+        int device;
+        const void* kernel;
+        int threads;
+        Residency r;
+    };
+    static std::mutex mu;
+    static std::vector<Entry> cache;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        for (const Entry& c : cache)
+            if (c.device == dev && c.kernel == kernel && c.threads == threads) {
+                *out = c.r;
+                return hipSuccess;
+            }
+    }
+    Residency r{0, 0};
+    if (kernel) {
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&r.per_cu, kernel, threads, 0);
+        if (e != hipSuccess) return e;
+    }
+    e = hipDeviceGetAttribute(&r.cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (r.cus < 1) r.cus = 1;
+    if (r.per_cu < 1) r.per_cu = 1;
+    std::lock_guard<std::mutex> lock(mu);
+    cache.push_back(Entry{dev, kernel, threads, r});
+    *out = r;
+    return hipSuccess;
+}
+
+// Launches one workgroup per token slot: at most two resident workgroups per
+// CU (more made no difference or ran slower on MI355X, whose 256 MB last-level
+// cache and HBM3E queues are already full with two), and never more than T.
+template <typename Args>
+hipError_t launch_persistent(void (*kernel)(Args, int64_t), const Args& a, int64_t T, int threads,
+                             hipStream_t stream) {
+    Residency r{};
+    hipError_t e = residency(reinterpret_cast<const void*>(kernel), threads, &r);
+    if (e != hipSuccess) return e;
+    const int64_t resident = (int64_t)r.cus * (r.per_cu < 2 ? r.per_cu : 2);
+    const int64_t grid = T < resident ? T : resident;
+    kernel<<<dim3((unsigned)grid), dim3((unsigned)threads), 0, stream>>>(a, T);
+    return hipGetLastError();
+}
+
 template <int VPT, int CH>
-void launch_epilogue_ch(const EpilogueArgs& a, EpilogueMode mode, dim3 grid, dim3 block,
-                        hipStream_t stream) {
-    switch (mode) {
-        case kModeNorm:
-            fused_epilogue_kernel<VPT, kModeNorm, CH><<<grid, block, 0, stream>>>(a);
-            break;
-        case kModeQuantToken:
-            fused_epilogue_kernel<VPT, kModeQuantToken, CH><<<grid, block, 0, stream>>>(a);
-            break;
-        default:
-            fused_epilogue_kernel<VPT, kModeQuantBlock, CH><<<grid, block, 0, stream>>>(a);
-            break;
+hipError_t launch_epilogue_ch(const EpilogueArgs& a, EpilogueMode mode, int64_t T, int threads,
+                              hipStream_t stream) {
+    if constexpr (VPT * CH > kMaxLoadsPerLane) {
+        return hipErrorInvalidValue;  // never picked: see pick_epilogue_shape
+    } else {
+        switch (mode) {
+            case kModeNorm:
+                return launch_persistent(fused_epilogue_kernel<VPT, kModeNorm, CH>, a, T, threads,
+                                         stream);
+            case kModeQuantToken:
+                return launch_persistent(fused_epilogue_kernel<VPT, kModeQuantToken, CH>, a, T,
+                                         threads, stream);
+            default:
+                return launch_persistent(fused_epilogue_kernel<VPT, kModeQuantBlock, CH>, a, T,
+                                         threads, stream);
+        }
     }
 }
 
 template <int VPT>
 hipError_t launch_epilogue_vpt(const EpilogueArgs& a, EpilogueMode mode, int64_t T, int threads,
-                               hipStream_t stream) {
-    const dim3 grid((unsigned)T), block((unsigned)threads);
-    // chunk of partial buffers loaded together: 2, 4 or 8
-    if (a.P <= 2) launch_epilogue_ch<VPT, 2>(a, mode, grid, block, stream);
-    else if (a.P <= 4) launch_epilogue_ch<VPT, 4>(a, mode, grid, block, stream);
-    else launch_epilogue_ch<VPT, 8>(a, mode, grid, block, stream);
-    return hipGetLastError();
+                               int ch, hipStream_t stream) {
+    switch (ch) {
+        case 2: return launch_epilogue_ch<VPT, 2>(a, mode, T, threads, stream);
+        case 4: return launch_epilogue_ch<VPT, 4>(a, mode, T, threads, stream);
+        default: return hipErrorInvalidValue;  // the pickers choose 2 or 4
+    }
 }
 
 template <int VPT>
 hipError_t launch_qk_vpt(const QkArgs& a, QkMode mode, int64_t T, int threads, hipStream_t stream) {
-    const dim3 grid((unsigned)T), block((unsigned)threads);
     switch (mode) {
-        case kQkLocal: qk_norm_kernel<VPT, kQkLocal><<<grid, block, 0, stream>>>(a); break;
-        case kQkSupplied: qk_norm_kernel<VPT, kQkSupplied><<<grid, block, 0, stream>>>(a); break;
-        default: qk_norm_kernel<VPT, kQkStats><<<grid, block, 0, stream>>>(a); break;
+        case kQkLocal: return launch_persistent(qk_norm_kernel<VPT, kQkLocal>, a, T, threads, stream);
+        case kQkSupplied:
+            return launch_persistent(qk_norm_kernel<VPT, kQkSupplied>, a, T, threads, stream);
+        default: return launch_persistent(qk_norm_kernel<VPT, kQkStats>, a, T, threads, stream);
     }
-    return hipGetLastError();
 }
 
 }  // namespace
 
-LaunchShape pick_shape(int nvec) {
-    // Fewest idle lanes first, then the workgroup size nearest 256 threads.
-    LaunchShape best{1, 64};
+namespace {
+
+// Among the allowed (vectors per lane, chunk) pairs: fewest idle lanes first,
+// then the workgroup size nearest 256 threads.
+template <class Allowed>
+LaunchShape pick(int nvec, int ch, Allowed max_threads) {
+    LaunchShape best{0, 0, ch};
     long best_waste = -1, best_dist = 0;
     for (int vpt = 1; vpt <= kMaxVpt; ++vpt) {
+        const int limit = max_threads(vpt);
+        if (limit <= 0) continue;
         const int lanes = (nvec + vpt - 1) / vpt;
         const int threads = ((lanes + kWave - 1) / kWave) * kWave;
-        if (threads > max_threads_for(vpt)) continue;
+        if (threads > limit) continue;
         const long waste = (long)threads * vpt - nvec;
         const long dist = threads > 256 ? threads - 256 : 256 - threads;
         if (best_waste < 0 || waste < best_waste || (waste == best_waste && dist < best_dist)) {
-            best = LaunchShape{vpt, threads};
+            best = LaunchShape{vpt, threads, ch};
             best_waste = waste;
             best_dist = dist;
         }
@@ -474,17 +661,64 @@ LaunchShape pick_shape(int nvec) {
     return best;
 }
 
+}  // namespace
+
+LaunchShape pick_epilogue_shape(int nvec, int P, int64_t T, int cus) {
+    if (T <= cus) {
+        // Fewer tokens than CUs: each token is one workgroup's whole job, so
+        // spread it over as many lanes as fit (fewest vectors per lane).
+        for (int ch = P <= 2 ? 2 : 4; ch >= 2; ch /= 2) {
+            for (int vpt = 1; vpt <= kMaxVpt && vpt * ch <= kMaxLoadsPerLane; ++vpt) {
+                const int threads = ((nvec + vpt - 1) / vpt + kWave - 1) / kWave * kWave;
+                if (threads <= max_threads_for(vpt, ch)) return LaunchShape{vpt, threads, ch};
+            }
+        }
+        return LaunchShape{0, 0, 0};
+    }
+    // Measured on MI355X (back-to-back launches, inputs out of cache): the
+    // fastest shapes for the 8192-wide prefill with 8 partials and the
+    // 7168-wide rows with 2 partials.
+    if (nvec == 1024 && P >= 3) return LaunchShape{3, 384, 2};
+    if (nvec == 896 && P <= 2) return LaunchShape{2, 448, 2};
+    // Otherwise: partials two at a time (as fast as four or eight at a time in
+    // those measurements, with fewer registers), fewest idle lanes, then the
+    // workgroup size nearest 256.
+    const LaunchShape s = pick(nvec, 2, [](int vpt) {
+        return vpt * 2 <= kMaxLoadsPerLane ? max_threads_for(vpt, 2) : 0;
+    });
+    return s.vpt > 0 ? s : LaunchShape{0, 0, 0};
+}
+
+LaunchShape pick_qk_shape(int nvec, int64_t T, int cus) {
+    if (T <= cus) {
+        for (int vpt = 1; vpt <= kMaxVpt; ++vpt) {
+            const int threads = ((nvec + vpt - 1) / vpt + kWave - 1) / kWave * kWave;
+            if (threads <= max_threads_for(vpt)) return LaunchShape{vpt, threads, 0};
+        }
+        return LaunchShape{0, 0, 0};
+    }
+    if (nvec == 896) return LaunchShape{4, 256, 0};  // q 6144 + k 1024, measured on MI355X
+    return pick(nvec, 0, [](int vpt) { return max_threads_for(vpt); });
+}
+
+hipError_t device_cus(int* cus) {
+    Residency r{};
+    hipError_t e = residency(nullptr, 0, &r);
+    *cus = r.cus;
+    return e;
+}
+
 hipError_t launch_epilogue(const EpilogueArgs& a, EpilogueMode mode, int64_t T, LaunchShape s,
                            hipStream_t stream) {
     switch (s.vpt) {
-        case 1: return launch_epilogue_vpt<1>(a, mode, T, s.threads, stream);
-        case 2: return launch_epilogue_vpt<2>(a, mode, T, s.threads, stream);
-        case 3: return launch_epilogue_vpt<3>(a, mode, T, s.threads, stream);
-        case 4: return launch_epilogue_vpt<4>(a, mode, T, s.threads, stream);
-        case 5: return launch_epilogue_vpt<5>(a, mode, T, s.threads, stream);
-        case 6: return launch_epilogue_vpt<6>(a, mode, T, s.threads, stream);
-        case 7: return launch_epilogue_vpt<7>(a, mode, T, s.threads, stream);
-        case 8: return launch_epilogue_vpt<8>(a, mode, T, s.threads, stream);
+        case 1: return launch_epilogue_vpt<1>(a, mode, T, s.threads, s.ch, stream);
+        case 2: return launch_epilogue_vpt<2>(a, mode, T, s.threads, s.ch, stream);
+        case 3: return launch_epilogue_vpt<3>(a, mode, T, s.threads, s.ch, stream);
+        case 4: return launch_epilogue_vpt<4>(a, mode, T, s.threads, s.ch, stream);
+        case 5: return launch_epilogue_vpt<5>(a, mode, T, s.threads, s.ch, stream);
+        case 6: return launch_epilogue_vpt<6>(a, mode, T, s.threads, s.ch, stream);
+        case 7: return launch_epilogue_vpt<7>(a, mode, T, s.threads, s.ch, stream);
+        case 8: return launch_epilogue_vpt<8>(a, mode, T, s.threads, s.ch, stream);
         default: return hipErrorInvalidValue;
     }
 }
