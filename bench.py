@@ -167,6 +167,32 @@ def device_copy(torch, dev):
     return round(2 * n * 2 / sec / 1e9, 1)
 
 
+def latency_shapes(fn, wl, torch, dev, reps=200):
+    """Average time per call of the two small workloads (16 x 1024 with P=1;
+    128 x 7168 with P=4), back to back on one stream. Their inputs fit in the
+    last-level cache, so these are latency figures, not HBM bandwidth."""
+    out = {}
+    for name in ("tiny", "decode"):
+        w = wl.WORKLOADS[name]
+        inp = wl.make_inputs(w)
+        parts = [p.to(dev) for p in inp.partials]
+        res, weight = inp.residual.to(dev), inp.weight.to(dev)
+        norm, rout = torch.empty_like(res), torch.empty_like(res)
+        for _ in range(10):
+            fn.fused_add_rmsnorm(parts, res, weight, w.eps, norm_out=norm, residual_out=rout)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn.fused_add_rmsnorm(parts, res, weight, w.eps, norm_out=norm, residual_out=rout)
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / reps
+        out[name] = {"T": w.T, "H": w.H, "P": w.P, "us_per_call": round(us, 2),
+                     "GB/s": round(w.algorithmic_bytes() / us / 1e3, 1), "cache_resident": True}
+        log(f"[bench] {name}: {us:.2f} us per call (cache-resident)")
+    return out
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -255,6 +281,7 @@ def main():
             "algorithmic_bytes_per_launch": dom.bytes,
         },
         "device_copy_GBs": device_copy(torch, dev),
+        "latency_shapes": latency_shapes(fn, wl, torch, dev),
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(parts)
