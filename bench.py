@@ -11,8 +11,11 @@ passes, so no launch finds its inputs in the 256 MB last-level cache.
 
 Prints ONE JSON line. ``value`` is the step's algorithmic bytes (each input
 read once, each output written once, weights once per launch) divided by the
-wall time of a step, in GB/s; ``roofline`` is the dominant kernel (the
-per-token FP8 epilogue) timed with HIP events on its launch stream;
+wall time of a step, in GB/s, with the step's four launches captured once in a
+HIP graph and replayed K times (``eager_*`` gives the same step launched from
+Python). ``per_launch`` and ``roofline`` come from a separate eager pass of K
+steps in which every launch is bracketed by HIP events on its stream; the
+roofline is the dominant kernel's (the per-token FP8 epilogue).
 ``cpu_baseline`` times the CPU oracle on one full step of the same inputs.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu-baseline]
@@ -167,10 +170,27 @@ def device_copy(torch, dev):
     return round(2 * n * 2 / sec / 1e9, 1)
 
 
-def latency_shapes(fn, wl, torch, dev, reps=200):
-    """Average time per call of the two small workloads (16 x 1024 with P=1;
-    128 x 7168 with P=4), back to back on one stream. Their inputs fit in the
-    last-level cache, so these are latency figures, not HBM bandwidth."""
+def capture(torch, fn_step):
+    """Captures fn_step() in a HIP graph (after one run on the capture stream to
+    warm the library's launch-shape cache). No memset nodes: the kernels write
+    every output element themselves."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn_step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn_step()
+    return g
+
+
+def latency_shapes(fn, wl, torch, dev, calls=50, reps=20):
+    """GPU time per call of the two small workloads (16 x 1024 with P=1;
+    128 x 7168 with P=4): `calls` back-to-back calls captured in one graph and
+    replayed. Their inputs fit in the last-level cache, so these are latency
+    figures, not HBM bandwidth."""
     out = {}
     for name in ("tiny", "decode"):
         w = wl.WORKLOADS[name]
@@ -178,18 +198,22 @@ def latency_shapes(fn, wl, torch, dev, reps=200):
         parts = [p.to(dev) for p in inp.partials]
         res, weight = inp.residual.to(dev), inp.weight.to(dev)
         norm, rout = torch.empty_like(res), torch.empty_like(res)
-        for _ in range(10):
-            fn.fused_add_rmsnorm(parts, res, weight, w.eps, norm_out=norm, residual_out=rout)
+
+        def many():
+            for _ in range(calls):
+                fn.fused_add_rmsnorm(parts, res, weight, w.eps, norm_out=norm, residual_out=rout)
+        g = capture(torch, many)
+        g.replay()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(reps):
-            fn.fused_add_rmsnorm(parts, res, weight, w.eps, norm_out=norm, residual_out=rout)
+            g.replay()
         b.record()
         torch.cuda.synchronize()
-        us = a.elapsed_time(b) * 1e3 / reps
+        us = a.elapsed_time(b) * 1e3 / (reps * calls)
         out[name] = {"T": w.T, "H": w.H, "P": w.P, "us_per_call": round(us, 2),
                      "GB/s": round(w.algorithmic_bytes() / us / 1e3, 1), "cache_resident": True}
-        log(f"[bench] {name}: {us:.2f} us per call (cache-resident)")
+        log(f"[bench] {name}: {us:.2f} us per call (graph replay, cache-resident)")
     return out
 
 
@@ -213,12 +237,17 @@ def main():
     parts = [Part(n, fn, wl, torch, dev) for n in STEP]
     torch.cuda.synchronize()
 
-    for _ in range(args.warmup):
+    def step():
         for p in parts:
             p.call()
-    torch.cuda.synchronize()
 
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
     K = args.steps
+
+    # Pass 1, eager: each launch bracketed by HIP events on the launch stream;
+    # gives the per-launch times and the dominant kernel's roofline.
     ev = {p.name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                    for _ in range(K)] for p in parts}
     torch.cuda.synchronize()
@@ -229,6 +258,18 @@ def main():
             s.record()
             p.call()
             e.record()
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) / K * 1e3
+
+    # Pass 2, the reported throughput: the step captured once in a HIP graph,
+    # K replays bracketed by synchronisation.
+    g = capture(torch, step)
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        g.replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
@@ -280,6 +321,8 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": dom.bytes,
         },
+        "eager_ms_per_step": round(eager_ms, 4),
+        "eager_GBs": round(step_bytes / (eager_ms / 1e3) / 1e9, 1),
         "device_copy_GBs": device_copy(torch, dev),
         "latency_shapes": latency_shapes(fn, wl, torch, dev),
     }

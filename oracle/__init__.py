@@ -66,6 +66,11 @@ def _load():
     lib.orc_qk_rmsnorm.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                    ctypes.c_int64, vp, vp, ctypes.c_float, ctypes.c_int,
                                    vp, vp, vp, vp, vp]
+    lib.orc_sharded_means.restype = ctypes.c_int
+    lib.orc_sharded_means.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, vp]
+    lib.orc_sharded_rmsnorm.restype = ctypes.c_int
+    lib.orc_sharded_rmsnorm.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, vp,
+                                        ctypes.c_float, ctypes.c_int, vp, vp, vp]
     _lib = lib
     return lib
 
@@ -239,7 +244,53 @@ def qk_rmsnorm(qkv: np.ndarray, q_size: int, kv_size: int, q_weight: np.ndarray,
     return out
 
 
+# ----------------------------------------------------------------------------- sharded-hidden RMSNorm
+
+def _rows(x: np.ndarray, H: int):
+    x = np.asarray(x)
+    if x.dtype != np.uint16 or x.ndim != 2:
+        raise TypeError("x must be uint16 [T, row]")
+    if x.strides[1] != 2:
+        raise ValueError("rows must be contiguous")
+    if x.shape[1] < H:
+        raise ValueError("row shorter than H")
+    T = x.shape[0]
+    return x, T, (x.strides[0] // 2 if T > 1 else x.shape[1])
+
+
+def sharded_means(x: np.ndarray, H: int) -> np.ndarray:
+    """Local means of squares [T] (fp64) of the first H channels of each row."""
+    x, T, stride = _rows(x, H)
+    out = np.empty((T,), np.float64)
+    rc = _load().orc_sharded_means(_ptr(x), T, stride, H, _ptr(out))
+    if rc != 0:
+        raise RuntimeError(f"oracle sharded_means failed with code {rc}")
+    return out
+
+
+def sharded_rmsnorm(x: np.ndarray, H: int, weight: np.ndarray, eps: float, tp_world: int = 1,
+                    var_in: Optional[np.ndarray] = None, want_pre: bool = False) -> dict:
+    """RMSNorm of this rank's H channels of each row; var_in (fp32 [T]) is the sum
+    of the ranks' local means, or None for local statistics (tp_world 1)."""
+    x, T, stride = _rows(x, H)
+    weight = _c(weight, np.uint16)
+    if var_in is not None:
+        var_in = _c(var_in, np.float32)
+        if var_in.shape != (T,):
+            raise ValueError("var_in must be fp32 [T]")
+    out = np.empty((T, H), np.uint16)
+    y = np.empty((T, H), np.float64) if want_pre else None
+    rc = _load().orc_sharded_rmsnorm(_ptr(x), T, stride, H, _ptr(weight), float(eps),
+                                     int(tp_world), _ptr(var_in), _ptr(out), _ptr(y))
+    if rc != 0:
+        raise RuntimeError(f"oracle sharded_rmsnorm failed with code {rc}")
+    res = {"out": out}
+    if want_pre:
+        res["y"] = y
+    return res
+
+
 __all__ = [
     "max_threads", "bf16_decode", "bf16_encode", "e4m3_decode", "e4m3_encode",
-    "fused_add_rmsnorm", "qk_means", "qk_rmsnorm",
+    "fused_add_rmsnorm", "qk_means", "qk_rmsnorm", "sharded_means", "sharded_rmsnorm",
 ]

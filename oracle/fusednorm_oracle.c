@@ -364,3 +364,62 @@ int orc_qk_rmsnorm(const uint16_t* qkv, int64_t T, int64_t row_stride, int64_t q
     }
     return ORC_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Sharded-hidden RMSNorm: one matrix whose hidden dimension is split over   */
+/* tp_world ranks ([TS-TRTLLM] "MiniMax QK fused AR + RMSNorm":              */
+/* minimax_allreduce_rms, the single-matrix form; the two stages around the  */
+/* all-reduce follow [VLLM-QK]). A token's row at x + t*row_stride holds this */
+/* rank's H_local channels.                                                   */
+/* ------------------------------------------------------------------------ */
+
+/* The pre stage: local mean of squares of each row, means[t] (fp64). */
+int orc_sharded_means(const uint16_t* x, int64_t T, int64_t row_stride, int64_t H,
+                      double* means) {
+    if (!x || !means || T < 0 || H <= 0 || row_stride < H) return ORC_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        const uint16_t* row = x + t * row_stride;
+        double ss = 0.0;
+        for (int64_t j = 0; j < H; ++j) {
+            double v = orc_bf16_decode(row[j]);
+            ss += v * v;
+        }
+        means[t] = ss / (double)H;
+    }
+    return ORC_OK;
+}
+
+/* The post stage: out = x * rsqrt(var / tp_world + eps) * w, where var is the
+ * local mean (var_in == NULL, tp_world must be 1) or var_in[t] = the sum over
+ * the tp_world ranks of their local means (fp32 [T]). out is contiguous
+ * [T, H]; y (fp64, nullable) exposes the values before rounding. */
+int orc_sharded_rmsnorm(const uint16_t* x, int64_t T, int64_t row_stride, int64_t H,
+                        const uint16_t* weight, float eps, int tp_world, const float* var_in,
+                        uint16_t* out, double* y) {
+    if (!x || !weight || !out || T < 0 || H <= 0 || row_stride < H || tp_world < 1 ||
+        (!var_in && tp_world != 1))
+        return ORC_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        const uint16_t* row = x + t * row_stride;
+        double var;
+        if (var_in) {
+            var = (double)var_in[t];
+        } else {
+            double ss = 0.0;
+            for (int64_t j = 0; j < H; ++j) {
+                double v = orc_bf16_decode(row[j]);
+                ss += v * v;
+            }
+            var = ss / (double)H;
+        }
+        double inv = 1.0 / sqrt(var / (double)tp_world + (double)eps);
+        for (int64_t j = 0; j < H; ++j) {
+            double v = orc_bf16_decode(row[j]) * inv * orc_bf16_decode(weight[j]);
+            out[t * H + j] = orc_bf16_encode(v);
+            if (y) y[t * H + j] = v;
+        }
+    }
+    return ORC_OK;
+}

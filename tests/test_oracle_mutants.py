@@ -18,7 +18,7 @@ from oracle import _build
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PIN_FILES = ["tests/test_oracle_codecs.py", "tests/test_oracle_norm.py",
-             "tests/test_oracle_quant.py", "tests/test_oracle_qk.py"]
+             "tests/test_oracle_quant.py", "tests/test_oracle_qk.py", "tests/test_oracle_sharded.py"]
 
 # (name, text in the source, replacement)
 MUTANTS = [
@@ -77,6 +77,14 @@ MUTANTS = [
      "vk = sk / (double)kv_size;", "vk = sk / (double)q_size;"),
     ("QK k output uses q's weight",
      "inv_k * orc_bf16_decode(k_weight[j])", "inv_k * orc_bf16_decode(q_weight[j])"),
+    ("sharded norm ignores tp_world",
+     "double inv = 1.0 / sqrt(var / (double)tp_world + (double)eps);",
+     "double inv = 1.0 / sqrt(var + (double)eps);"),
+    ("sharded means over H - 1",
+     "means[t] = ss / (double)H;", "means[t] = ss / (double)(H - 1);"),
+    ("sharded norm eps outside the sqrt",
+     "double inv = 1.0 / sqrt(var / (double)tp_world + (double)eps);",
+     "double inv = 1.0 / (sqrt(var / (double)tp_world) + (double)eps);"),
 ]
 
 

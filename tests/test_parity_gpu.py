@@ -351,3 +351,121 @@ def test_qk_empty_and_invalid(fn):
     qkv = torch.zeros(4, 96, dtype=torch.bfloat16, device=DEV)
     with pytest.raises(fn.FusedNormError):
         fn.qk_rmsnorm(qkv, 48, 16, w, w[:16].contiguous(), tp_world=4)
+
+
+# ----------------------------------------------------------------------------- persistent loop
+
+@pytest.mark.parametrize("mode", list(MODES))
+@pytest.mark.parametrize("H,P", [(8, 1), (1024, 3), (4104, 8), (7168, 2), (8192, 8), (16384, 16),
+                                 (1152, 5), (2048, 12)])
+def test_many_tokens_per_workgroup(fn, mode, H, P):
+    """T well above the number of resident workgroups (at most 2 per CU), so each
+    workgroup handles several tokens and prefetches across them."""
+    if mode == "quant_block" and H % 128:
+        pytest.skip("block FP8 needs H % 128 == 0")
+    T = 1100 if H <= 8192 else 700
+    inp = norm_case(T, H, P, mode, outliers=0.002, seed=H + P)
+    check(run_gpu(fn, inp, mode), run_oracle(inp, mode), mode, label=f"{mode} T={T} H={H} P={P}")
+
+
+@pytest.mark.parametrize("q,k,stride,supplied", [(6144, 1024, 8192, False), (6144, 1024, 8192, True),
+                                                 (48, 16, 96, False), (1024, 128, 1280, True)])
+def test_qk_many_tokens_per_workgroup(fn, q, k, stride, supplied):
+    T = 1500
+    g = torch.Generator().manual_seed(q + stride)
+    base = torch.randn(T, stride, generator=g).to(torch.bfloat16)
+    base[:, q + k:] = float("nan")
+    wq = (1 + 0.1 * torch.randn(q, generator=g)).to(torch.bfloat16)
+    wk = (1 + 0.1 * torch.randn(k, generator=g)).to(torch.bfloat16)
+    b = wl.bits(base)
+    var_in, tp = (None, 1) if not supplied else ((oracle.qk_means(b, q, k) * 2).astype(np.float32), 2)
+    qo, ko = fn.qk_rmsnorm(base.to(DEV), q, k, wq.to(DEV), wk.to(DEV), EPS, tp,
+                           None if var_in is None else torch.from_numpy(var_in).to(DEV))
+    var = fn.qk_rmsnorm_var(base.to(DEV), q, k)
+    torch.cuda.synchronize()
+    ref = oracle.qk_rmsnorm(b, q, k, wl.bits(wq), wl.bits(wk), EPS, tp, var_in)
+    compare_bf16(u16(qo), ref["q"], what="q_out")
+    compare_bf16(u16(ko), ref["k"], what="k_out")
+    compare_scales(var.cpu().numpy(), oracle.qk_means(b, q, k), what="local means")
+
+
+def test_concurrent_calls_from_two_threads(fn):
+    import threading
+    inps = [norm_case(700, 7168, 2, "quant_block", seed=s) for s in (1, 2)]
+    refs = [run_oracle(i, "quant_block") for i in inps]
+    errors = []
+
+    def worker(k):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for _ in range(10):
+                    out = run_gpu(fn, inps[k], "quant_block")
+            s.synchronize()
+            check(out, refs[k], "quant_block", label=f"thread {k}")
+        except Exception as e:  # surfaced below
+            errors.append(e)
+
+    ts = [threading.Thread(target=worker, args=(k,)) for k in (0, 1)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert not errors, errors
+
+
+def test_graph_capture_replays_match_eager(fn):
+    """The four launches of a benchmark step captured in a HIP graph: every replay,
+    interleaved with eager work and synchronisation, equals the eager result."""
+    c = norm_case(1100, 8192, 8, "quant_token", outliers=0.001, seed=5)
+    b = norm_case(1100, 7168, 2, "quant_block", seed=6)
+    wq = wl.WORKLOADS["qk_local"]
+    qk = wl.make_inputs(wq, T=1100)
+    dev_c = ([p.to(DEV) for p in c.partials], c.residual.to(DEV), c.weight.to(DEV))
+    dev_b = ([p.to(DEV) for p in b.partials], b.residual.to(DEV), b.weight.to(DEV))
+    qkv, wqq, wkk = qk.qkv.to(DEV), qk.q_weight.to(DEV), qk.k_weight.to(DEV)
+    outs = dict(
+        c=(torch.empty_like(dev_c[1]), torch.empty(1100, 8192, dtype=torch.uint8, device=DEV),
+           torch.empty(1100, device=DEV)),
+        b=(torch.empty_like(dev_b[1]), torch.empty(1100, 7168, dtype=torch.uint8, device=DEV),
+           torch.empty(1100, 56, device=DEV)),
+        qk=(torch.empty(1100, 6144, dtype=torch.bfloat16, device=DEV),
+            torch.empty(1100, 1024, dtype=torch.bfloat16, device=DEV)))
+
+    def step():
+        fn.fused_add_rmsnorm_quant_fp8(*dev_c, 1e-6, residual_out=outs["c"][0],
+                                       quant_out=outs["c"][1], scale_out=outs["c"][2])
+        fn.qk_rmsnorm(qkv, wq.q_size, wq.kv_size, wqq, wkk, 1e-6, q_out=outs["qk"][0],
+                      k_out=outs["qk"][1])
+        fn.fused_add_rmsnorm_quant_fp8_block(*dev_b, 1e-6, residual_out=outs["b"][0],
+                                             quant_out=outs["b"][1], scale_out=outs["b"][2])
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return [t.clone() for v in outs.values() for t in v]
+
+    def clear():
+        for v in outs.values():
+            for t in v:
+                t.zero_()
+
+    step()
+    eager = snapshot()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()                                     # warm the launch-shape cache off-capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for k in range(4):
+        clear()
+        torch.cuda.synchronize()
+        g.replay()
+        got = snapshot()
+        for a, e in zip(got, eager):
+            assert torch.equal(a, e), f"replay {k} differs from the eager result"
+        step()                                     # eager work between replays
+        torch.cuda.synchronize()
