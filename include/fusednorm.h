@@ -182,6 +182,35 @@ int qk_rmsnorm_var(const void* qkv, int64_t T, int64_t row_stride, int64_t q_siz
                    int64_t kv_size, float* var_out, void* stream);
 
 /*
+ * sharded_rmsnorm -- RMSNorm of one matrix whose hidden dimension is split over
+ * tp_world ranks: the single-matrix form of the MiniMax norm ([TS-TRTLLM]
+ * "MiniMax QK fused AR + RMSNorm": minimax_allreduce_rms, input [T, H/nranks]
+ * with a bf16 weight of that width), computed as the post stage that follows
+ * the all-reduce of the ranks' local means ([VLLM-QK] structure). Per token:
+ *   var    = var_in[t]            if var_in != NULL (the sum of the ranks' local means)
+ *          = mean(x[t,:]^2) (fp32) if var_in == NULL (tp_world must be 1)
+ *   out[t,:] = bf16( x[t,:] * rsqrt(var / tp_world + eps) * weight )
+ *
+ *   x             bf16 rows at x + t*row_stride, 16-B aligned; H and row_stride
+ *                 multiples of 8, H <= row_stride, H <= 16384
+ *   weight        bf16 [H];  var_in fp32 [T], 4-B aligned, or NULL
+ *   out           bf16 [T, H] contiguous
+ */
+int sharded_rmsnorm(const void* x, int64_t T, int64_t row_stride, int64_t H, const void* weight,
+                    float eps, int tp_world, const float* var_in, void* out, void* stream);
+
+/*
+ * sharded_rmsnorm_var -- the pre stage of sharded_rmsnorm ([VLLM-QK]
+ * _minimax_qk_var_kernel's form for one segment): var_out[t] = mean(x[t,:H]^2),
+ * accumulated in fp32. Summing var_out over the ranks (the all-reduce, not part
+ * of this library) gives sharded_rmsnorm's var_in.
+ *
+ *   var_out       fp32 [T], 4-B aligned
+ */
+int sharded_rmsnorm_var(const void* x, int64_t T, int64_t row_stride, int64_t H, float* var_out,
+                        void* stream);
+
+/*
  * fusednorm_e4m3_encode -- element-wise fp32 -> OCP E4M3 with exactly the
  * conversion the FP8 epilogues use (clamp to [-448, 448], round to nearest,
  * ties to even, sign kept, so a negative value that rounds to zero is 0x80).

@@ -66,6 +66,10 @@ def _load():
     lib.orc_qk_rmsnorm.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                    ctypes.c_int64, vp, vp, ctypes.c_float, ctypes.c_int,
                                    vp, vp, vp, vp, vp]
+    lib.orc_fused_add_rmsnorm_static.restype = ctypes.c_int
+    lib.orc_fused_add_rmsnorm_static.argtypes = [
+        ctypes.POINTER(vp), ctypes.c_int, vp, vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
+        ctypes.c_float, vp, vp, vp, vp, vp, vp]
     lib.orc_sharded_means.restype = ctypes.c_int
     lib.orc_sharded_means.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, vp]
     lib.orc_sharded_rmsnorm.restype = ctypes.c_int
@@ -188,6 +192,39 @@ def fused_add_rmsnorm(partials: Sequence[np.ndarray], residual: np.ndarray, weig
     return out
 
 
+def fused_add_rmsnorm_static(partials: Sequence[np.ndarray], residual: np.ndarray,
+                             weight: np.ndarray, eps: float, scale: float, *,
+                             want_norm: bool = True, want_pre: bool = False) -> dict:
+    """The fused epilogue with one static fp32 FP8 scale s for the whole tensor:
+    codes = e4m3(clamp(y / s)). Returns ``residual``, ``norm`` (or None),
+    ``codes``, ``near_tie`` and with want_pre ``y`` and ``r`` (= y / s)."""
+    lib = _load()
+    parts = [_c(p, np.uint16) for p in partials]
+    residual = _c(residual, np.uint16)
+    weight = _c(weight, np.uint16)
+    T, H = residual.shape
+    for p in parts:
+        if p.shape != (T, H):
+            raise ValueError("partials must match residual's shape")
+    arr = (ctypes.c_void_p * len(parts))(*[p.ctypes.data for p in parts])
+    res_out = np.empty((T, H), np.uint16)
+    norm_out = np.empty((T, H), np.uint16) if want_norm else None
+    codes = np.empty((T, H), np.uint8)
+    tie = np.empty((T, H), np.uint8)
+    y = np.empty((T, H), np.float64) if want_pre else None
+    r = np.empty((T, H), np.float64) if want_pre else None
+    rc = lib.orc_fused_add_rmsnorm_static(arr, len(parts), _ptr(residual), _ptr(weight), T, H,
+                                          float(eps), float(scale), _ptr(norm_out),
+                                          _ptr(res_out), _ptr(codes), _ptr(tie), _ptr(y),
+                                          _ptr(r))
+    if rc != 0:
+        raise RuntimeError(f"oracle fused_add_rmsnorm_static failed with code {rc}")
+    out = {"residual": res_out, "norm": norm_out, "codes": codes, "near_tie": tie.astype(bool)}
+    if want_pre:
+        out.update(y=y, r=r)
+    return out
+
+
 # ----------------------------------------------------------------------------- QK norm
 
 def _qk_view(qkv: np.ndarray, q_size: int, kv_size: int):
@@ -292,5 +329,6 @@ def sharded_rmsnorm(x: np.ndarray, H: int, weight: np.ndarray, eps: float, tp_wo
 
 __all__ = [
     "max_threads", "bf16_decode", "bf16_encode", "e4m3_decode", "e4m3_encode",
-    "fused_add_rmsnorm", "qk_means", "qk_rmsnorm", "sharded_means", "sharded_rmsnorm",
+    "fused_add_rmsnorm", "fused_add_rmsnorm_static", "qk_means", "qk_rmsnorm", "sharded_means",
+    "sharded_rmsnorm",
 ]

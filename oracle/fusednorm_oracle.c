@@ -423,3 +423,49 @@ int orc_sharded_rmsnorm(const uint16_t* x, int64_t T, int64_t row_stride, int64_
     }
     return ORC_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Fused epilogue with a static FP8 scale: the scale_factor argument of       */
+/* [TS-TRTLLM] "AllReduce fusion" (one fp32 value for the whole tensor). The */
+/* pages do not say whether it multiplies or divides; as for the dynamic     */
+/* variants it is taken as the dequantisation multiplier, y ~ code * s, so   */
+/* the quantised value is y / s, clamped to +-448 and rounded to the nearest */
+/* e4m3 code (ties to even). No scale is written.                            */
+/* ------------------------------------------------------------------------ */
+int orc_fused_add_rmsnorm_static(const uint16_t* const* partials, int P, const uint16_t* residual,
+                                 const uint16_t* weight, int64_t T, int64_t H, float eps,
+                                 float scale, uint16_t* norm_out, uint16_t* residual_out,
+                                 uint8_t* codes, uint8_t* near_tie, double* y_out,
+                                 double* r_out) {
+    if (orc_check_common(partials, P, residual, weight, T, H) != ORC_OK) return ORC_ERR_ARG;
+    if (!codes || !(scale > 0.0f) || isinf(scale)) return ORC_ERR_ARG;
+    const double s = (double)scale;
+    int err = ORC_OK;
+#pragma omp parallel
+    {
+        float* x = (float*)malloc((size_t)H * sizeof(float));
+        if (!x) {
+#pragma omp atomic write
+            err = ORC_ERR_NOMEM;
+        }
+#pragma omp for schedule(static)
+        for (int64_t t = 0; t < T; ++t) {
+            if (!x) continue;
+            int64_t off = t * H;
+            orc_row_sum(partials, P, residual, off, H, x);
+            double inv = orc_row_inv_rms(x, H, eps);
+            for (int64_t j = 0; j < H; ++j) {
+                double y = (double)x[j] * inv * orc_bf16_decode(weight[j]);
+                double r = y / s;
+                if (residual_out) residual_out[off + j] = orc_bf16_encode((double)x[j]);
+                if (norm_out) norm_out[off + j] = orc_bf16_encode(y);
+                codes[off + j] = orc_e4m3_encode(r);
+                if (near_tie) near_tie[off + j] = orc_e4m3_near_tie(r);
+                if (y_out) y_out[off + j] = y;
+                if (r_out) r_out[off + j] = r;
+            }
+        }
+        free(x);
+    }
+    return err;
+}

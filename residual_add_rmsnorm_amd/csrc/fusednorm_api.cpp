@@ -248,8 +248,9 @@ int qk_common(const void* qkv, int64_t T, int64_t row_stride, int64_t q_size, in
     a.wk = static_cast<const u32x4*>(k_weight);
     a.q_out = static_cast<u32x4*>(q_out);
     a.k_out = static_cast<u32x4*>(k_out);
-    a.var_in = reinterpret_cast<const float2*>(var_in);
-    a.var_out = reinterpret_cast<float2*>(var_out);
+    a.var_in = var_in;
+    a.var_out = var_out;
+    a.segments = 2;
     a.nq = (int)(q_size / 8);
     a.nk = (int)(kv_size / 8);
     a.q_size = (float)q_size;
@@ -263,6 +264,79 @@ int qk_common(const void* qkv, int64_t T, int64_t row_stride, int64_t q_size, in
     const fusednorm::LaunchShape shape = fusednorm::pick_qk_shape(a.nq + a.nk, T, cus);
     if (shape.vpt == 0)
         return fail(FUSEDNORM_ERR_UNSUPPORTED, "no launch shape covers q_size + kv_size");
+    return hip_status(fusednorm::launch_qk(a, mode, T, shape, (hipStream_t)stream), "kernel launch");
+}
+
+int sharded_common(const void* x, int64_t T, int64_t row_stride, int64_t H, const void* weight,
+                   float eps, int tp_world, const float* var_in, void* out, float* var_out,
+                   void* stream, fusednorm::QkMode mode) {
+    const bool stats = mode == fusednorm::kQkStats;
+    if (T < 0) return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "T = %lld < 0", (long long)T);
+    if (H <= 0) return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "H = %lld <= 0", (long long)H);
+    if (row_stride <= 0) return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "row_stride must be > 0");
+    if (!stats) {
+        if (int s = check_eps(eps)) return s;
+        if (tp_world < 1) return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "tp_world = %d < 1", tp_world);
+        if (!var_in && tp_world != 1)
+            return fail(FUSEDNORM_ERR_INVALID_ARGUMENT,
+                        "tp_world = %d needs var_in (the sum of the ranks' means)", tp_world);
+    }
+    if (H % 8 || row_stride % 8)
+        return fail(FUSEDNORM_ERR_UNSUPPORTED, "H and row_stride must be multiples of 8");
+    if (row_stride < H)
+        return fail(FUSEDNORM_ERR_UNSUPPORTED, "row_stride %lld < H", (long long)row_stride);
+    if (H > FUSEDNORM_MAX_HIDDEN)
+        return fail(FUSEDNORM_ERR_UNSUPPORTED, "H = %lld above %d", (long long)H, FUSEDNORM_MAX_HIDDEN);
+    if (T > 0x7FFFFFFF) return fail(FUSEDNORM_ERR_UNSUPPORTED, "T above 2^31 - 1");
+    if (T == 0) return ok();  // nothing to read or write: buffers are not examined
+    if (!x) return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "x is NULL");
+    if (stats) {
+        if (!var_out) return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "var_out is NULL");
+        if (!aligned(var_out, 4)) return fail(FUSEDNORM_ERR_UNSUPPORTED, "var_out not 4-byte aligned");
+    } else {
+        if (!weight) return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "weight is NULL");
+        if (!out) return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "out is NULL");
+        if (!aligned(weight, 16) || !aligned(out, 16))
+            return fail(FUSEDNORM_ERR_UNSUPPORTED, "weight / out not 16-byte aligned");
+        if (var_in && !aligned(var_in, 4))
+            return fail(FUSEDNORM_ERR_UNSUPPORTED, "var_in not 4-byte aligned");
+    }
+    if (!aligned(x, 16)) return fail(FUSEDNORM_ERR_UNSUPPORTED, "x not 16-byte aligned");
+    Span in[3];
+    int n_in = 0;
+    in[n_in++] = span(x, ((T - 1) * row_stride + H) * 2, "x");
+    Span o[1];
+    if (stats) {
+        o[0] = span(var_out, T * 4, "var_out");
+    } else {
+        in[n_in++] = span(weight, H * 2, "weight");
+        if (var_in) in[n_in++] = span(var_in, T * 4, "var_in");
+        o[0] = span(out, T * H * 2, "out");
+    }
+    if (int s = check_overlaps(in, n_in, o, 1, -1, -1)) return s;
+
+    fusednorm::QkArgs a{};
+    a.qkv = static_cast<const uint16_t*>(x);
+    a.row_stride = row_stride;
+    a.wq = static_cast<const u32x4*>(weight);
+    a.wk = static_cast<const u32x4*>(weight);
+    a.q_out = static_cast<u32x4*>(out);
+    a.k_out = nullptr;
+    a.var_in = var_in;
+    a.var_out = var_out;
+    a.segments = 1;
+    a.nq = (int)(H / 8);
+    a.nk = 0;
+    a.q_size = (float)H;
+    a.kv_size = 1.0f;
+    a.tp_world = (float)tp_world;
+    a.eps = eps;
+    if (!stats) mode = var_in ? fusednorm::kQkSupplied : fusednorm::kQkLocal;
+    (void)hipGetLastError();
+    int cus = 0;
+    if (hipError_t e = fusednorm::device_cus(&cus)) return hip_status(e, "device query");
+    const fusednorm::LaunchShape shape = fusednorm::pick_qk_shape(a.nq, T, cus);
+    if (shape.vpt == 0) return fail(FUSEDNORM_ERR_UNSUPPORTED, "no launch shape covers H");
     return hip_status(fusednorm::launch_qk(a, mode, T, shape, (hipStream_t)stream), "kernel launch");
 }
 
@@ -305,6 +379,18 @@ int qk_rmsnorm_var(const void* qkv, int64_t T, int64_t row_stride, int64_t q_siz
                    int64_t kv_size, float* var_out, void* stream) {
     return qk_common(qkv, T, row_stride, q_size, kv_size, nullptr, nullptr, 0.0f, 1, nullptr,
                      nullptr, nullptr, var_out, stream, fusednorm::kQkStats);
+}
+
+int sharded_rmsnorm(const void* x, int64_t T, int64_t row_stride, int64_t H, const void* weight,
+                    float eps, int tp_world, const float* var_in, void* out, void* stream) {
+    return sharded_common(x, T, row_stride, H, weight, eps, tp_world, var_in, out, nullptr, stream,
+                          fusednorm::kQkLocal);
+}
+
+int sharded_rmsnorm_var(const void* x, int64_t T, int64_t row_stride, int64_t H, float* var_out,
+                        void* stream) {
+    return sharded_common(x, T, row_stride, H, nullptr, 0.0f, 1, nullptr, nullptr, var_out, stream,
+                          fusednorm::kQkStats);
 }
 
 int fusednorm_e4m3_encode(const float* in, void* out, int64_t n, void* stream) {

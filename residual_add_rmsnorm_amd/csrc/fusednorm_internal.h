@@ -48,19 +48,22 @@ struct EpilogueArgs {
     float eps;
 };
 
+// The QK norm and its one-segment form (sharded-hidden RMSNorm): each row holds
+// segment 1 (q, nq vectors) then, when segments == 2, segment 2 (k, nk vectors).
 struct QkArgs {
-    const uint16_t* qkv;                  // bf16 rows: q | k | v
+    const uint16_t* qkv;                  // bf16 rows
     int64_t row_stride;                   // elements
     const u32x4* wq;                      // bf16 [q_size]
-    const u32x4* wk;                      // bf16 [kv_size]
+    const u32x4* wk;                      // bf16 [kv_size] (segments == 2)
     u32x4* q_out;                         // bf16 [T, q_size]
-    u32x4* k_out;                         // bf16 [T, kv_size]
-    const float2* var_in;                 // fp32 [T, 2] (supplied mode)
-    float2* var_out;                      // fp32 [T, 2] (statistics mode)
+    u32x4* k_out;                         // bf16 [T, kv_size] (segments == 2)
+    const float* var_in;                  // fp32 [T, segments] (supplied mode)
+    float* var_out;                       // fp32 [T, segments] (statistics mode)
+    int segments;                         // 1 or 2
     int nq;                               // q_size / 8
-    int nk;                               // kv_size / 8
+    int nk;                               // kv_size / 8 (0 when segments == 1)
     float q_size;
-    float kv_size;
+    float kv_size;                        // 1 when segments == 1 (unused)
     float tp_world;
     float eps;
 };

@@ -450,13 +450,17 @@ __global__ void __launch_bounds__(max_threads_for(VPT)) qk_norm_kernel(QkArgs a,
     int64_t t = blockIdx.x;  // the host launches at most T workgroups
     u32x4 next[VPT];
     float2 next_var = make_float2(0.0f, 0.0f);
+    const int seg = a.segments;
     const uint32_t qk_bytes = (uint32_t)nv * 16u;  // q and k; v is never read
     {
         const Row src = make_row(a.qkv + t * a.row_stride, qk_bytes);
 #pragma unroll
         for (int s = 0; s < VPT; ++s) next[s] = load16(src, off[s]);
     }
-    if (MODE == kQkSupplied) next_var = a.var_in[t];
+    if (MODE == kQkSupplied) {
+        next_var.x = a.var_in[t * seg];
+        if (seg == 2) next_var.y = a.var_in[t * seg + 1];
+    }
 
     for (int parity = 0;; parity ^= 1) {
         u32x4 raw[VPT];
@@ -469,7 +473,10 @@ __global__ void __launch_bounds__(max_threads_for(VPT)) qk_norm_kernel(QkArgs a,
             const Row src = make_row(a.qkv + t_next * a.row_stride, qk_bytes);
 #pragma unroll
             for (int s = 0; s < VPT; ++s) next[s] = load16(src, off[s]);
-            if (MODE == kQkSupplied) next_var = a.var_in[t_next];
+            if (MODE == kQkSupplied) {
+                next_var.x = a.var_in[t_next * seg];
+                if (seg == 2) next_var.y = a.var_in[t_next * seg + 1];
+            }
         }
 
         float var_q, var_k;
@@ -492,12 +499,17 @@ __global__ void __launch_bounds__(max_threads_for(VPT)) qk_norm_kernel(QkArgs a,
             var_k = tk / a.kv_size;
         }
         if (MODE == kQkStats) {
-            if (tid == 0) a.var_out[t] = make_float2(var_q, var_k);
+            if (tid == 0) {
+                a.var_out[t * seg] = var_q;
+                if (seg == 2) a.var_out[t * seg + 1] = var_k;
+            }
         } else {
             const float inv_q = rsqrtf(var_q / a.tp_world + a.eps);
             const float inv_k = rsqrtf(var_k / a.tp_world + a.eps);
             const Row out_q = make_row(a.q_out + t * a.nq, (uint32_t)a.nq * 16u);
-            const Row out_k = make_row(a.k_out + t * a.nk, (uint32_t)a.nk * 16u);
+            // one segment: the k resource covers zero bytes, so every k store is dropped
+            const Row out_k = seg == 2 ? make_row(a.k_out + t * a.nk, (uint32_t)a.nk * 16u)
+                                       : make_row(a.q_out, 0u);
 #pragma unroll
             for (int s = 0; s < VPT; ++s) {
                 const float inv = is_q[s] ? inv_q : inv_k;

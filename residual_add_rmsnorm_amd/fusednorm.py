@@ -57,6 +57,8 @@ def _load() -> ctypes.CDLL:
                                               vp, vp],
         "qk_rmsnorm": [vp, i64, i64, i64, i64, vp, vp, f32, i32, vp, vp, vp, vp],
         "qk_rmsnorm_var": [vp, i64, i64, i64, i64, vp, vp],
+        "sharded_rmsnorm": [vp, i64, i64, i64, vp, f32, i32, vp, vp, vp],
+        "sharded_rmsnorm_var": [vp, i64, i64, i64, vp, vp],
         "fusednorm_e4m3_encode": [vp, vp, i64, vp],
     }
     for name, args in sig.items():
@@ -261,7 +263,7 @@ def _qkv_layout(qkv: torch.Tensor):
 
 
 def _check_qk_shapes(qkv, q_size, kv_size, tensors) -> None:
-    if q_size <= 0 or kv_size <= 0 or qkv.shape[1] < q_size + kv_size:
+    if q_size <= 0 or kv_size < 0 or qkv.shape[1] < q_size + kv_size:
         raise ValueError(f"qkv rows ({qkv.shape[1]}) must hold q_size + kv_size "
                          f"({q_size} + {kv_size})")
     if qkv.shape[0] > 1 and qkv.stride(0) < q_size + kv_size:
@@ -312,6 +314,42 @@ def qk_rmsnorm_var(qkv: torch.Tensor, q_size: int, kv_size: int,
     return var_out
 
 
+def sharded_rmsnorm(x: torch.Tensor, weight: torch.Tensor, eps: float = 1e-6, tp_world: int = 1,
+                    var_in: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                    H: Optional[int] = None, stream=None) -> torch.Tensor:
+    """RMSNorm of this rank's share of a hidden-sharded matrix: the first H
+    (default: all) channels of each row of x (rows may be strided). var_in is the
+    fp32 [T] sum of the ranks' local means (from sharded_rmsnorm_var plus an
+    all-reduce), or None for local statistics. Returns contiguous [T, H]."""
+    T, row_stride = _qkv_layout(x)
+    H = x.shape[1] if H is None else int(H)
+    _need(weight, "weight")
+    if var_in is not None:
+        _need(var_in, "var_in", dtype=torch.float32)
+    out = torch.empty(T, H, dtype=x.dtype, device=x.device) if out is None else out
+    _need(out, "out")
+    _check_qk_shapes(x, H, 0, [("weight", weight, (H,)), ("var_in", var_in, (T,)),
+                               ("out", out, (T, H))])
+    _check("sharded_rmsnorm", _lib.sharded_rmsnorm(
+        _ptr(x), T, row_stride, H, _ptr(weight), float(eps), int(tp_world), _ptr(var_in),
+        _ptr(out), _stream(x.device, stream)))
+    return out
+
+
+def sharded_rmsnorm_var(x: torch.Tensor, H: Optional[int] = None,
+                        var_out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Local mean of squares of the first H channels of each row: fp32 [T]."""
+    T, row_stride = _qkv_layout(x)
+    H = x.shape[1] if H is None else int(H)
+    var_out = (torch.empty(T, dtype=torch.float32, device=x.device)
+               if var_out is None else var_out)
+    _need(var_out, "var_out", dtype=torch.float32)
+    _check_qk_shapes(x, H, 0, [("var_out", var_out, (T,))])
+    _check("sharded_rmsnorm_var", _lib.sharded_rmsnorm_var(
+        _ptr(x), T, row_stride, H, _ptr(var_out), _stream(x.device, stream)))
+    return var_out
+
+
 def e4m3_encode(x: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """fp32 -> OCP e4m3 with the FP8 epilogues' own conversion (saturating, RNE)."""
     _need(x, "x", dtype=torch.float32)
@@ -326,6 +364,7 @@ def e4m3_encode(x: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None
 
 __all__ = [
     "fused_add_rmsnorm", "fused_add_rmsnorm_quant_fp8", "fused_add_rmsnorm_quant_fp8_block",
-    "qk_rmsnorm", "qk_rmsnorm_var", "e4m3_encode", "version", "library_path",
+    "qk_rmsnorm", "qk_rmsnorm_var", "sharded_rmsnorm", "sharded_rmsnorm_var", "e4m3_encode",
+    "version", "library_path",
     "FusedNormError", "FusedNormUnsupported", "FusedNormLibraryMissing",
 ]

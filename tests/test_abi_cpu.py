@@ -46,7 +46,7 @@ def test_header_declares_the_entry_points():
     assert {"fused_add_rmsnorm", "fused_add_rmsnorm_quant_fp8",
             "fused_add_rmsnorm_quant_fp8_block", "qk_rmsnorm", "qk_rmsnorm_var",
             "fusednorm_e4m3_encode", "fusednorm_status_string", "fusednorm_last_error",
-            "fusednorm_version"} <= names
+            "fusednorm_version", "sharded_rmsnorm", "sharded_rmsnorm_var"} <= names
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -218,3 +218,26 @@ def test_binding_fails_loudly_without_the_library(tmp_path):
                        capture_output=True, text=True)
     assert r.returncode != 0
     assert "FusedNormLibraryMissing" in r.stderr
+
+
+def test_sharded_validation(lib):
+    sr, sv = lib.sharded_rmsnorm, lib.sharded_rmsnorm_var
+    v = ctypes.cast(addr(5), ctypes.c_void_p)
+
+    def call(T=4, stride=64, H=64, eps=1e-6, tp=1, var=None, x=None, out=None):
+        return sr(x or addr(1), T, stride, H, addr(2), eps, tp, var, out or addr(6), None)
+
+    assert call(T=0) == 0
+    assert call(tp=2) == 1 and "needs var_in" in last(lib)
+    assert call(H=0) == 1
+    assert call(H=60, stride=64) == 2
+    assert call(H=72, stride=64) == 2 and "row_stride" in last(lib)
+    assert call(H=16392, stride=16392) == 2
+    assert call(eps=float("nan")) == 1
+    assert call(x=addr(1, 8)) == 2
+    assert call(out=addr(1, 32)) == 2 and "overlaps" in last(lib)
+    assert call(var=ctypes.c_void_p(A + 5 * MB * 64 + 2), tp=2) == 2
+    assert call(T=0, var=v, tp=4) == 0
+    assert sv(addr(1), 4, 64, 64, None, None) == 1
+    assert sv(addr(1), 4, 64, 64, ctypes.cast(addr(1), ctypes.c_void_p), None) == 2
+    assert sv(addr(1), 0, 64, 64, None, None) == 0

@@ -18,7 +18,8 @@ from oracle import _build
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PIN_FILES = ["tests/test_oracle_codecs.py", "tests/test_oracle_norm.py",
-             "tests/test_oracle_quant.py", "tests/test_oracle_qk.py", "tests/test_oracle_sharded.py"]
+             "tests/test_oracle_quant.py", "tests/test_oracle_qk.py", "tests/test_oracle_sharded.py",
+             "tests/test_oracle_static.py"]
 
 # (name, text in the source, replacement)
 MUTANTS = [
@@ -77,6 +78,11 @@ MUTANTS = [
      "vk = sk / (double)kv_size;", "vk = sk / (double)q_size;"),
     ("QK k output uses q's weight",
      "inv_k * orc_bf16_decode(k_weight[j])", "inv_k * orc_bf16_decode(q_weight[j])"),
+    ("static scale multiplies instead of dividing",
+     "double r = y / s;", "double r = y * s;"),
+    ("static codes from bf16(y)",
+     "codes[off + j] = orc_e4m3_encode(r);",
+     "codes[off + j] = orc_e4m3_encode(orc_bf16_decode(orc_bf16_encode(y)) / s);"),
     ("sharded norm ignores tp_world",
      "double inv = 1.0 / sqrt(var / (double)tp_world + (double)eps);",
      "double inv = 1.0 / sqrt(var + (double)eps);"),

@@ -469,3 +469,34 @@ def test_graph_capture_replays_match_eager(fn):
             assert torch.equal(a, e), f"replay {k} differs from the eager result"
         step()                                     # eager work between replays
         torch.cuda.synchronize()
+
+
+
+# ----------------------------------------------------------------------------- sharded-hidden RMSNorm
+
+@pytest.mark.parametrize("T", [1, 37, 1500])
+@pytest.mark.parametrize("H,stride", [(8, 8), (1536, 1536), (1536, 6144), (2048, 2112),
+                                      (6144, 8192), (16384, 16384)])
+def test_sharded_rmsnorm(fn, T, H, stride):
+    tp = 4
+    g = torch.Generator().manual_seed(H + T + stride)
+    shards = [torch.randn(T, stride, generator=g).to(torch.bfloat16) for _ in range(tp)]
+    for s_ in shards:
+        s_[:, H:] = float("nan")                            # past the shard's width: never read
+    w = (1 + 0.1 * torch.randn(H, generator=g)).to(torch.bfloat16)
+    bits = [wl.bits(s_) for s_ in shards]
+    # pre stage on every rank, then the all-reduce (a sum) and the post stage on rank 0
+    dev_shards = [s_.to(DEV) for s_ in shards]
+    var = [fn.sharded_rmsnorm_var(d, H=H) for d in dev_shards]
+    torch.cuda.synchronize()
+    for b, v in zip(bits, var):
+        compare_scales(v.cpu().numpy(), oracle.sharded_means(b, H), what="local means")
+    var_in = sum(oracle.sharded_means(b, H) for b in bits).astype(np.float32)
+    out = fn.sharded_rmsnorm(dev_shards[0], w.to(DEV), EPS, tp, torch.from_numpy(var_in).to(DEV),
+                             H=H)
+    local = fn.sharded_rmsnorm(dev_shards[0], w.to(DEV), EPS, H=H)
+    torch.cuda.synchronize()
+    ref = oracle.sharded_rmsnorm(bits[0], H, wl.bits(w), EPS, tp, var_in)
+    ref_local = oracle.sharded_rmsnorm(bits[0], H, wl.bits(w), EPS)
+    compare_bf16(u16(out), ref["out"], what="sharded out")
+    compare_bf16(u16(local), ref_local["out"], what="local out")
