@@ -138,6 +138,25 @@ int fused_add_rmsnorm_quant_fp8_block(const void* const* partials, int P,
                                       void* stream);
 
 /*
+ * fused_add_rmsnorm_quant_fp8_static -- pattern kARResidualRMSNormFP8Quant with
+ * the static fp32 scale_factor of [TS-TRTLLM] "AllReduce fusion" (one value for
+ * the whole tensor; with norm_out != NULL also kARResidualRMSNormOutFP8Quant).
+ * The scale is the dequantisation multiplier, as for the dynamic variants:
+ *   quant_out[t,j] = e4m3( clamp(y[t,j] / scale, -448, 448) ), nearest, ties to even
+ * with y as in fused_add_rmsnorm_quant_fp8; no scale is written.
+ *
+ *   scale_factor  DEVICE pointer to one fp32, 4-B aligned; must be finite and > 0
+ *                 (read by the kernel, so the host cannot check its value)
+ *   norm_out      bf16 [T, H] or NULL;  quant_out e4m3 [T, H], 16-B aligned
+ * Other arguments as for fused_add_rmsnorm.
+ */
+int fused_add_rmsnorm_quant_fp8_static(const void* const* partials, int P,
+                                       const void* residual_in, const void* weight, int64_t T,
+                                       int64_t H, float eps, const float* scale_factor,
+                                       void* norm_out, void* residual_out, void* quant_out,
+                                       void* stream);
+
+/*
  * qk_rmsnorm -- the MiniMax QK RMSNorm under tensor parallelism ([VLLM-QK]
  * _minimax_qk_norm_tp_eager and _minimax_rms_apply_kernel; [TS-TRTLLM]
  * minimax_allreduce_rms_qk for the contiguous outputs).

@@ -85,11 +85,12 @@ int hip_status(hipError_t e, const char* what) {
     return ok();
 }
 
-enum class Quant { None, Token, Block };
+enum class Quant { None, Token, Block, Static };
 
 int fused_common(const void* const* partials, int P, const void* residual_in, const void* weight,
                  int64_t T, int64_t H, float eps, int group_size, void* norm_out,
-                 void* residual_out, void* quant_out, float* scale_out, void* stream, Quant quant) {
+                 void* residual_out, void* quant_out, float* scale_out, void* stream, Quant quant,
+                 const float* static_scale = nullptr) {
     // ---- scalar arguments
     if (P < 1 || P > FUSEDNORM_MAX_PARTIALS)
         return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "P = %d outside [1, %d]", P,
@@ -123,8 +124,12 @@ int fused_common(const void* const* partials, int P, const void* residual_in, co
         return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "norm_out is NULL");
     if (quant != Quant::None && !quant_out)
         return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "quant_out is NULL");
-    if (quant != Quant::None && !scale_out)
+    if ((quant == Quant::Token || quant == Quant::Block) && !scale_out)
         return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "scale_out is NULL");
+    if (quant == Quant::Static && !static_scale)
+        return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "scale_factor is NULL");
+    if (static_scale && !aligned(static_scale, 4))
+        return fail(FUSEDNORM_ERR_UNSUPPORTED, "scale_factor not 4-byte aligned");
     for (int p = 0; p < P; ++p)
         if (!aligned(partials[p], 16))
             return fail(FUSEDNORM_ERR_UNSUPPORTED, "partials[%d] not 16-byte aligned", p);
@@ -136,7 +141,7 @@ int fused_common(const void* const* partials, int P, const void* residual_in, co
     if (scale_out && !aligned(scale_out, 4)) return fail(FUSEDNORM_ERR_UNSUPPORTED, "scale_out not 4-byte aligned");
     // ---- buffer overlap
     const int64_t row_bytes = H * 2;
-    Span in[FUSEDNORM_MAX_PARTIALS + 2];
+    Span in[FUSEDNORM_MAX_PARTIALS + 3];
     int n_in = 0;
     for (int p = 0; p < P; ++p) in[n_in++] = span(partials[p], T * row_bytes, "a partial");
     const int residual_idx = n_in;
@@ -146,8 +151,9 @@ int fused_common(const void* const* partials, int P, const void* residual_in, co
     int n_out = 0;
     out[n_out++] = span(residual_out, T * row_bytes, "residual_out");
     if (norm_out) out[n_out++] = span(norm_out, T * row_bytes, "norm_out");
-    if (quant != Quant::None) {
-        out[n_out++] = span(quant_out, T * H, "quant_out");
+    if (quant == Quant::Static) in[n_in++] = span(static_scale, 4, "scale_factor");
+    if (quant != Quant::None) out[n_out++] = span(quant_out, T * H, "quant_out");
+    if (quant == Quant::Token || quant == Quant::Block) {
         const int64_t scales = quant == Quant::Token ? T : T * (H / FUSEDNORM_FP8_GROUP);
         out[n_out++] = span(scale_out, scales * 4, "scale_out");
     }
@@ -162,6 +168,7 @@ int fused_common(const void* const* partials, int P, const void* residual_in, co
     a.norm_out = static_cast<u32x4*>(norm_out);
     a.quant_out = static_cast<u32x2*>(quant_out);
     a.scale_out = scale_out;
+    a.static_scale = static_scale;
     a.P = P;
     a.nvec = (int)(H / 8);
     a.row_bytes = (uint32_t)(H * 2);
@@ -170,7 +177,8 @@ int fused_common(const void* const* partials, int P, const void* residual_in, co
     a.eps = eps;
     const fusednorm::EpilogueMode mode = quant == Quant::None    ? fusednorm::kModeNorm
                                          : quant == Quant::Token ? fusednorm::kModeQuantToken
-                                                                 : fusednorm::kModeQuantBlock;
+                                         : quant == Quant::Block ? fusednorm::kModeQuantBlock
+                                                                 : fusednorm::kModeQuantStatic;
     (void)hipGetLastError();  // start from a clean error state
     int cus = 0;
     if (hipError_t e = fusednorm::device_cus(&cus)) return hip_status(e, "device query");
@@ -366,6 +374,15 @@ int fused_add_rmsnorm_quant_fp8_block(const void* const* partials, int P,
                                       void* stream) {
     return fused_common(partials, P, residual_in, weight, T, H, eps, group_size, norm_out,
                         residual_out, quant_out, scale_out, stream, Quant::Block);
+}
+
+int fused_add_rmsnorm_quant_fp8_static(const void* const* partials, int P,
+                                       const void* residual_in, const void* weight, int64_t T,
+                                       int64_t H, float eps, const float* scale_factor,
+                                       void* norm_out, void* residual_out, void* quant_out,
+                                       void* stream) {
+    return fused_common(partials, P, residual_in, weight, T, H, eps, 0, norm_out, residual_out,
+                        quant_out, nullptr, stream, Quant::Static, scale_factor);
 }
 
 int qk_rmsnorm(const void* qkv, int64_t T, int64_t row_stride, int64_t q_size, int64_t kv_size,

@@ -29,7 +29,7 @@ constexpr __host__ __device__ int max_threads_for(int vpt, int ch) {
     return (vpt <= 2 && vpt * ch <= 8) ? 1024 : (vpt <= 4 ? 512 : 256);
 }
 
-enum EpilogueMode { kModeNorm = 0, kModeQuantToken = 1, kModeQuantBlock = 2 };
+enum EpilogueMode { kModeNorm = 0, kModeQuantToken = 1, kModeQuantBlock = 2, kModeQuantStatic = 3 };
 enum QkMode { kQkLocal = 0, kQkSupplied = 1, kQkStats = 2 };
 
 struct EpilogueArgs {
@@ -39,7 +39,8 @@ struct EpilogueArgs {
     u32x4* residual_out;                  // bf16 [T, H]
     u32x4* norm_out;                      // bf16 [T, H] or null
     u32x2* quant_out;                     // e4m3 [T, H] (FP8 modes)
-    float* scale_out;                     // fp32 [T] or [T, H/128] (FP8 modes)
+    float* scale_out;                     // fp32 [T] or [T, H/128] (dynamic FP8 modes)
+    const float* static_scale;            // fp32 [1] (static FP8 mode)
     int P;
     int nvec;                             // H / 8
     uint32_t row_bytes;                   // H * 2

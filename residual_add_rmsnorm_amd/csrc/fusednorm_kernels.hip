@@ -342,6 +342,9 @@ fused_epilogue_kernel(EpilogueArgs a, int64_t T) {
         wv[s] = valid[s] ? a.weight[i] : zero4();
     }
 
+    // static FP8: one dequantisation scale s for the tensor; codes from y * (1/s)
+    const float static_rcp = MODE == kModeQuantStatic ? 1.0f / *a.static_scale : 0.0f;
+
     int64_t t = blockIdx.x;  // the host launches at most T workgroups
     TokenLoads<VPT, CH> L;
     issue_token_loads(a, n0, t * a.nvec, off, L);
@@ -407,7 +410,12 @@ fused_epilogue_kernel(EpilogueArgs a, int64_t T) {
                 for (int e = 0; e < 8; ++e) y[e] = (x[s][e] * inv) * w[e];
                 store16(out_norm, off[s], pack_bf16x8(y));
             }
-            if (MODE != kModeNorm) {
+            if (MODE == kModeQuantStatic) {
+                float r[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) r[e] = ((x[s][e] * inv) * w[e]) * static_rcp;
+                store8(out_q, off[s] / 2u, pack_e4m3x8(r));
+            } else if (MODE != kModeNorm) {
                 float r[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) r[e] = (xw[e] * q.pre) * q.qmul;
@@ -619,8 +627,11 @@ hipError_t launch_epilogue_ch(const EpilogueArgs& a, EpilogueMode mode, int64_t 
             case kModeQuantToken:
                 return launch_persistent(fused_epilogue_kernel<VPT, kModeQuantToken, CH>, a, T,
                                          threads, stream);
-            default:
+            case kModeQuantBlock:
                 return launch_persistent(fused_epilogue_kernel<VPT, kModeQuantBlock, CH>, a, T,
+                                         threads, stream);
+            default:
+                return launch_persistent(fused_epilogue_kernel<VPT, kModeQuantStatic, CH>, a, T,
                                          threads, stream);
         }
     }

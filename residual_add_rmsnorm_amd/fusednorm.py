@@ -55,6 +55,8 @@ def _load() -> ctypes.CDLL:
         "fused_add_rmsnorm_quant_fp8": [vpp, i32, vp, vp, i64, i64, f32, vp, vp, vp, vp, vp],
         "fused_add_rmsnorm_quant_fp8_block": [vpp, i32, vp, vp, i64, i64, f32, i32, vp, vp, vp,
                                               vp, vp],
+        "fused_add_rmsnorm_quant_fp8_static": [vpp, i32, vp, vp, i64, i64, f32, vp, vp, vp, vp,
+                                               vp],
         "qk_rmsnorm": [vp, i64, i64, i64, i64, vp, vp, f32, i32, vp, vp, vp, vp],
         "qk_rmsnorm_var": [vp, i64, i64, i64, i64, vp, vp],
         "sharded_rmsnorm": [vp, i64, i64, i64, vp, f32, i32, vp, vp, vp],
@@ -252,6 +254,38 @@ def fused_add_rmsnorm_quant_fp8_block(partials, residual: torch.Tensor, weight: 
     return quant_out, scale_out, residual_out, norm_out
 
 
+def fused_add_rmsnorm_quant_fp8_static(partials, residual: torch.Tensor, weight: torch.Tensor,
+                                       scale_factor: Union[torch.Tensor, float],
+                                       eps: float = 1e-6, norm_out: Optional[torch.Tensor] = None,
+                                       residual_out: Optional[torch.Tensor] = None,
+                                       quant_out: Optional[torch.Tensor] = None, stream=None):
+    """Fused epilogue + OCP e4m3 with one static dequantisation scale for the
+    tensor (a float or a one-element fp32 GPU tensor, as the pages accept).
+    Returns (quant_out e4m3 [T,H], residual_out, norm_out or None)."""
+    parts, arr = _partials(partials)
+    _need(residual, "residual")
+    _need(weight, "weight")
+    T, H = residual.shape
+    if not isinstance(scale_factor, torch.Tensor):
+        scale_factor = torch.tensor([float(scale_factor)], dtype=torch.float32,
+                                    device=residual.device)
+    _need(scale_factor, "scale_factor", dtype=torch.float32)
+    if scale_factor.numel() != 1:
+        raise ValueError("scale_factor must hold one value")
+    residual_out = torch.empty_like(residual) if residual_out is None else residual_out
+    quant_out = _fp8_out(residual) if quant_out is None else quant_out
+    _need(residual_out, "residual_out")
+    _need(quant_out, "quant_out", dtype=None)
+    if norm_out is not None:
+        _need(norm_out, "norm_out")
+    _check_norm_shapes(parts, residual, weight, norm_out, residual_out, quant_out)
+    _same_device([("scale_factor", scale_factor)], residual.device)
+    _check("fused_add_rmsnorm_quant_fp8_static", _lib.fused_add_rmsnorm_quant_fp8_static(
+        arr, len(parts), _ptr(residual), _ptr(weight), T, H, float(eps), _ptr(scale_factor),
+        _ptr(norm_out), _ptr(residual_out), _ptr(quant_out), _stream(residual.device, stream)))
+    return quant_out, residual_out, norm_out
+
+
 def _qkv_layout(qkv: torch.Tensor):
     if not isinstance(qkv, torch.Tensor) or not qkv.is_cuda or qkv.dtype != torch.bfloat16:
         raise TypeError("qkv must be a bf16 GPU tensor")
@@ -364,6 +398,7 @@ def e4m3_encode(x: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None
 
 __all__ = [
     "fused_add_rmsnorm", "fused_add_rmsnorm_quant_fp8", "fused_add_rmsnorm_quant_fp8_block",
+    "fused_add_rmsnorm_quant_fp8_static",
     "qk_rmsnorm", "qk_rmsnorm_var", "sharded_rmsnorm", "sharded_rmsnorm_var", "e4m3_encode",
     "version", "library_path",
     "FusedNormError", "FusedNormUnsupported", "FusedNormLibraryMissing",

@@ -46,7 +46,8 @@ def test_header_declares_the_entry_points():
     assert {"fused_add_rmsnorm", "fused_add_rmsnorm_quant_fp8",
             "fused_add_rmsnorm_quant_fp8_block", "qk_rmsnorm", "qk_rmsnorm_var",
             "fusednorm_e4m3_encode", "fusednorm_status_string", "fusednorm_last_error",
-            "fusednorm_version", "sharded_rmsnorm", "sharded_rmsnorm_var"} <= names
+            "fusednorm_version", "sharded_rmsnorm", "sharded_rmsnorm_var",
+            "fused_add_rmsnorm_quant_fp8_static"} <= names
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -241,3 +242,17 @@ def test_sharded_validation(lib):
     assert sv(addr(1), 4, 64, 64, None, None) == 1
     assert sv(addr(1), 4, 64, 64, ctypes.cast(addr(1), ctypes.c_void_p), None) == 2
     assert sv(addr(1), 0, 64, 64, None, None) == 0
+
+
+def test_static_quant_validation(lib):
+    fs = lib.fused_add_rmsnorm_quant_fp8_static
+    sc = ctypes.cast(addr(6), ctypes.c_void_p)
+    assert fs(parts(2), 2, addr(1), addr(2), 0, 64, 1e-6, sc, None, addr(4), addr(5), None) == 0
+    assert fs(parts(2), 2, addr(1), addr(2), 4, 64, 1e-6, None, None, addr(4), addr(5), None) == 1
+    assert "scale_factor" in last(lib)
+    assert fs(parts(2), 2, addr(1), addr(2), 4, 64, 1e-6, sc, None, addr(4), None, None) == 1
+    assert fs(parts(2), 2, addr(1), addr(2), 4, 64, 1e-6, ctypes.c_void_p(A + 6 * MB * 64 + 2),
+              None, addr(4), addr(5), None) == 2
+    # the scale may not sit inside an output
+    assert fs(parts(2), 2, addr(1), addr(2), 4, 64, 1e-6, ctypes.c_void_p(A + 5 * MB * 64 + 64),
+              None, addr(4), addr(5), None) == 2

@@ -500,3 +500,28 @@ def test_sharded_rmsnorm(fn, T, H, stride):
     ref_local = oracle.sharded_rmsnorm(bits[0], H, wl.bits(w), EPS)
     compare_bf16(u16(out), ref["out"], what="sharded out")
     compare_bf16(u16(local), ref_local["out"], what="local out")
+
+
+
+# ----------------------------------------------------------------------------- static FP8 scale
+
+@pytest.mark.parametrize("T,H,P", [(7, 1024, 1), (37, 7168, 2), (1100, 8192, 8), (300, 16384, 16),
+                                   (600, 4104, 3)])
+@pytest.mark.parametrize("scale", [0.004, 0.02, 1.0])
+@pytest.mark.parametrize("want_norm", [False, True])
+def test_static_scale_quant(fn, T, H, P, scale, want_norm):
+    inp = norm_case(T, H, P, "quant_token", outliers=0.002, seed=H + P + T)
+    parts = [p.to(DEV) for p in inp.partials]
+    res, w = inp.residual.to(DEV), inp.weight.to(DEV)
+    norm = torch.empty_like(res) if want_norm else None
+    q, rout, norm = fn.fused_add_rmsnorm_quant_fp8_static(parts, res, w, scale, EPS,
+                                                          norm_out=norm)
+    torch.cuda.synchronize()
+    ref = oracle.fused_add_rmsnorm_static([wl.bits(p) for p in inp.partials],
+                                          wl.bits(inp.residual), wl.bits(inp.weight), EPS, scale,
+                                          want_norm=want_norm)
+    compare_bf16(u16(rout), ref["residual"], max_ulp=0, what="residual_out")
+    if want_norm:
+        compare_bf16(u16(norm), ref["norm"], what="norm_out")
+    say(f"static s={scale} T={T} H={H} P={P}:",
+        compare_e4m3(u8(q), ref["codes"], ref["near_tie"]))
