@@ -157,6 +157,34 @@ int fused_add_rmsnorm_quant_fp8_static(const void* const* partials, int P,
                                        void* stream);
 
 /*
+ * fused_rs_epilogue -- the epilogue of a reduce-scatter fusion
+ * ([TS-TRTLLM] "ReduceScatter fusion": trtllm_reducescatter_fusion; pattern
+ * codes from ReduceScatterFusionPattern in "Pattern enums") on this GPU's
+ * token slice. Rows [token_offset, token_offset + T) of the P partial buffers
+ * are summed in fp32 in partial order, then add_in (patterns 7, 8) and the
+ * residual are added, in that order; then RMSNorm and the pattern's step:
+ *   1 kRSResidualRMSNorm                     norm_out (required)
+ *   2 kRSResidualRMSNormFP8Quant             quant_out with the static scale_factor
+ *   4 kRSResidualRMSNormOutFP8Quant          as 2, plus norm_out (required)
+ *   6 kRSResidualRMSNormFP8BlockWiseQuant    quant_out + scale_out [T, H/128], norm_out optional
+ *   7 kRSAddResidualRMSNormFP8BlockWiseQuant as 6, with add_in
+ *   8 kRSAddResidualRMSNorm                  as 1, with add_in
+ * Patterns 0 (the bare collective) and 3, 5 (FP4) return FUSEDNORM_ERR_UNSUPPORTED.
+ *
+ *   partials      HOST array of P device pointers, each bf16 [token_num, H] with
+ *                 token_num >= token_offset + T (the caller guarantees it)
+ *   add_in        bf16 [T, H] for patterns 7 and 8, else NULL; P <= 15 with add_in
+ *   residual_in, residual_out, norm_out, quant_out  [T, H] of this slice
+ *   scale_factor  DEVICE fp32 [1] for patterns 2 and 4 (as
+ *                 fused_add_rmsnorm_quant_fp8_static), else ignored
+ * Other arguments as for fused_add_rmsnorm and its FP8 variants.
+ */
+int fused_rs_epilogue(int pattern, const void* const* partials, int P, int64_t token_offset,
+                      const void* add_in, const void* residual_in, const void* weight, int64_t T,
+                      int64_t H, float eps, const float* scale_factor, void* norm_out,
+                      void* residual_out, void* quant_out, float* scale_out, void* stream);
+
+/*
  * qk_rmsnorm -- the MiniMax QK RMSNorm under tensor parallelism ([VLLM-QK]
  * _minimax_qk_norm_tp_eager and _minimax_rms_apply_kernel; [TS-TRTLLM]
  * minimax_allreduce_rms_qk for the contiguous outputs).

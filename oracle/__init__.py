@@ -225,6 +225,48 @@ def fused_add_rmsnorm_static(partials: Sequence[np.ndarray], residual: np.ndarra
     return out
 
 
+# ----------------------------------------------------------------------------- reduce-scatter epilogue
+
+# Codes of ReduceScatterFusionPattern (tokenspeed trtllm.py page, section
+# "Pattern enums") that this epilogue implements.
+RS_RESIDUAL_RMSNORM = 1
+RS_RESIDUAL_RMSNORM_FP8 = 2
+RS_RESIDUAL_RMSNORM_OUT_FP8 = 4
+RS_RESIDUAL_RMSNORM_FP8_BLOCK = 6
+RS_ADD_RESIDUAL_RMSNORM_FP8_BLOCK = 7
+RS_ADD_RESIDUAL_RMSNORM = 8
+
+
+def rs_epilogue(pattern: int, partials: Sequence[np.ndarray], token_offset: int,
+                add_in: Optional[np.ndarray], residual: np.ndarray, weight: np.ndarray,
+                eps: float, scale_factor: Optional[float] = None) -> dict:
+    """The epilogue of trtllm_reducescatter_fusion (tokenspeed trtllm.py page,
+    section "ReduceScatter fusion") for one rank's token slice: rows
+    [token_offset, token_offset + T_local) of the P partial buffers (each
+    [token_num, H]) are summed in fp32 in partial order, then add_in (patterns
+    7 and 8) and the residual are added, in that order; then RMSNorm and the
+    pattern's FP8 step (2 and 4: the static scale_factor; 6 and 7: 1x128
+    groups). The reduced slice is the same arithmetic as the all-reduce
+    epilogue with add_in as one more addend after the partials."""
+    T = residual.shape[0]
+    rows = [np.ascontiguousarray(np.asarray(p)[token_offset:token_offset + T]) for p in partials]
+    if any(r.shape != residual.shape for r in rows):
+        raise ValueError("the token slice runs past a partial buffer")
+    needs_add = pattern in (RS_ADD_RESIDUAL_RMSNORM, RS_ADD_RESIDUAL_RMSNORM_FP8_BLOCK)
+    if needs_add != (add_in is not None):
+        raise ValueError("add_in is given exactly for patterns 7 and 8")
+    if add_in is not None:
+        rows.append(_c(add_in, np.uint16))
+    if pattern in (RS_RESIDUAL_RMSNORM, RS_ADD_RESIDUAL_RMSNORM):
+        return fused_add_rmsnorm(rows, residual, weight, eps)
+    if pattern in (RS_RESIDUAL_RMSNORM_FP8, RS_RESIDUAL_RMSNORM_OUT_FP8):
+        return fused_add_rmsnorm_static(rows, residual, weight, eps, scale_factor,
+                                        want_norm=pattern == RS_RESIDUAL_RMSNORM_OUT_FP8)
+    if pattern in (RS_RESIDUAL_RMSNORM_FP8_BLOCK, RS_ADD_RESIDUAL_RMSNORM_FP8_BLOCK):
+        return fused_add_rmsnorm(rows, residual, weight, eps, quant="block", want_norm=False)
+    raise ValueError(f"pattern {pattern} is not implemented")
+
+
 # ----------------------------------------------------------------------------- QK norm
 
 def _qk_view(qkv: np.ndarray, q_size: int, kv_size: int):
@@ -329,6 +371,6 @@ def sharded_rmsnorm(x: np.ndarray, H: int, weight: np.ndarray, eps: float, tp_wo
 
 __all__ = [
     "max_threads", "bf16_decode", "bf16_encode", "e4m3_decode", "e4m3_encode",
-    "fused_add_rmsnorm", "fused_add_rmsnorm_static", "qk_means", "qk_rmsnorm", "sharded_means",
-    "sharded_rmsnorm",
+    "fused_add_rmsnorm", "fused_add_rmsnorm_static", "rs_epilogue", "qk_means", "qk_rmsnorm",
+    "sharded_means", "sharded_rmsnorm",
 ]

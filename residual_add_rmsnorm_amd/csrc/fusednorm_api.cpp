@@ -87,10 +87,11 @@ int hip_status(hipError_t e, const char* what) {
 
 enum class Quant { None, Token, Block, Static };
 
-int fused_common(const void* const* partials, int P, const void* residual_in, const void* weight,
+int fused_common(const void* const* partials_in, int P, const void* residual_in, const void* weight,
                  int64_t T, int64_t H, float eps, int group_size, void* norm_out,
                  void* residual_out, void* quant_out, float* scale_out, void* stream, Quant quant,
-                 const float* static_scale = nullptr) {
+                 const float* static_scale = nullptr, int64_t token_offset = 0,
+                 const void* add_in = nullptr) {
     // ---- scalar arguments
     if (P < 1 || P > FUSEDNORM_MAX_PARTIALS)
         return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "P = %d outside [1, %d]", P,
@@ -112,11 +113,21 @@ int fused_common(const void* const* partials, int P, const void* residual_in, co
             return fail(FUSEDNORM_ERR_UNSUPPORTED, "H = %lld is not a multiple of %d",
                         (long long)H, FUSEDNORM_FP8_GROUP);
     }
+    if (token_offset < 0) return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "token_offset < 0");
+    if (add_in && P + 1 > FUSEDNORM_MAX_PARTIALS)
+        return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "P = %d leaves no room for add_in (at most %d)",
+                    P, FUSEDNORM_MAX_PARTIALS - 1);
     if (T == 0) return ok();  // nothing to read or write: buffers are not examined
     // ---- buffers
-    if (!partials) return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "partials is NULL");
+    if (!partials_in) return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "partials is NULL");
     for (int p = 0; p < P; ++p)
-        if (!partials[p]) return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "partials[%d] is NULL", p);
+        if (!partials_in[p]) return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "partials[%d] is NULL", p);
+    // The rows the kernel reads: each partial from token_offset on, then add_in as
+    // one more addend after the partials (before the residual).
+    const void* partials[FUSEDNORM_MAX_PARTIALS];
+    for (int p = 0; p < P; ++p)
+        partials[p] = static_cast<const char*>(partials_in[p]) + token_offset * H * 2;
+    if (add_in) partials[P++] = add_in;
     if (!residual_in) return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "residual_in is NULL");
     if (!weight) return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "weight is NULL");
     if (!residual_out) return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "residual_out is NULL");
@@ -143,7 +154,8 @@ int fused_common(const void* const* partials, int P, const void* residual_in, co
     const int64_t row_bytes = H * 2;
     Span in[FUSEDNORM_MAX_PARTIALS + 3];
     int n_in = 0;
-    for (int p = 0; p < P; ++p) in[n_in++] = span(partials[p], T * row_bytes, "a partial");
+    for (int p = 0; p < P; ++p)
+        in[n_in++] = span(partials[p], T * row_bytes, add_in && p == P - 1 ? "add_in" : "a partial");
     const int residual_idx = n_in;
     in[n_in++] = span(residual_in, T * row_bytes, "residual_in");
     in[n_in++] = span(weight, row_bytes, "weight");
@@ -383,6 +395,41 @@ int fused_add_rmsnorm_quant_fp8_static(const void* const* partials, int P,
                                        void* stream) {
     return fused_common(partials, P, residual_in, weight, T, H, eps, 0, norm_out, residual_out,
                         quant_out, nullptr, stream, Quant::Static, scale_factor);
+}
+
+int fused_rs_epilogue(int pattern, const void* const* partials, int P, int64_t token_offset,
+                      const void* add_in, const void* residual_in, const void* weight, int64_t T,
+                      int64_t H, float eps, const float* scale_factor, void* norm_out,
+                      void* residual_out, void* quant_out, float* scale_out, void* stream) {
+    const bool add = pattern == 7 || pattern == 8;
+    if (pattern == 0 || pattern == 3 || pattern == 5)
+        return fail(FUSEDNORM_ERR_UNSUPPORTED, "pattern %d is not implemented", pattern);
+    if (pattern < 0 || pattern > 8)
+        return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "pattern %d is not a reduce-scatter pattern",
+                    pattern);
+    if (T > 0 && add != (add_in != nullptr))
+        return fail(FUSEDNORM_ERR_INVALID_ARGUMENT,
+                    add ? "pattern %d needs add_in" : "pattern %d takes no add_in", pattern);
+    switch (pattern) {
+        case 1:
+        case 8:
+            return fused_common(partials, P, residual_in, weight, T, H, eps, 0, norm_out,
+                                residual_out, nullptr, nullptr, stream, Quant::None, nullptr,
+                                token_offset, add_in);
+        case 2:
+        case 4:
+            if (pattern == 2 && norm_out)
+                return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "pattern 2 writes no norm_out");
+            if (pattern == 4 && !norm_out && T > 0)
+                return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "pattern 4 needs norm_out");
+            return fused_common(partials, P, residual_in, weight, T, H, eps, 0, norm_out,
+                                residual_out, quant_out, nullptr, stream, Quant::Static,
+                                scale_factor, token_offset, add_in);
+        default:  // 6 and 7: 1x128 block FP8
+            return fused_common(partials, P, residual_in, weight, T, H, eps, FUSEDNORM_FP8_GROUP,
+                                norm_out, residual_out, quant_out, scale_out, stream, Quant::Block,
+                                nullptr, token_offset, add_in);
+    }
 }
 
 int qk_rmsnorm(const void* qkv, int64_t T, int64_t row_stride, int64_t q_size, int64_t kv_size,

@@ -57,6 +57,8 @@ def _load() -> ctypes.CDLL:
                                               vp, vp],
         "fused_add_rmsnorm_quant_fp8_static": [vpp, i32, vp, vp, i64, i64, f32, vp, vp, vp, vp,
                                                vp],
+        "fused_rs_epilogue": [i32, vpp, i32, i64, vp, vp, vp, i64, i64, f32, vp, vp, vp, vp, vp,
+                              vp],
         "qk_rmsnorm": [vp, i64, i64, i64, i64, vp, vp, f32, i32, vp, vp, vp, vp],
         "qk_rmsnorm_var": [vp, i64, i64, i64, i64, vp, vp],
         "sharded_rmsnorm": [vp, i64, i64, i64, vp, f32, i32, vp, vp, vp],
@@ -286,6 +288,73 @@ def fused_add_rmsnorm_quant_fp8_static(partials, residual: torch.Tensor, weight:
     return quant_out, residual_out, norm_out
 
 
+RS_PATTERNS = {1: "norm", 2: "static", 4: "static+norm", 6: "block", 7: "block", 8: "norm"}
+
+
+def fused_rs_epilogue(pattern: int, partials, token_offset: int, residual: torch.Tensor,
+                      weight: torch.Tensor, eps: float = 1e-6,
+                      add_in: Optional[torch.Tensor] = None, scale_factor=None,
+                      norm_out: Optional[torch.Tensor] = None,
+                      residual_out: Optional[torch.Tensor] = None,
+                      quant_out: Optional[torch.Tensor] = None,
+                      scale_out: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Reduce-scatter epilogue on rows [token_offset, token_offset + T) of the
+    partial buffers (each [token_num, H]); T = residual.shape[0]. Returns a dict
+    with the outputs the pattern writes."""
+    if pattern not in RS_PATTERNS:
+        raise FusedNormUnsupported("fused_rs_epilogue", FUSEDNORM_ERR_UNSUPPORTED,
+                                   f"pattern {pattern} is not implemented")
+    parts, arr = _partials(partials)
+    _need(residual, "residual")
+    _need(weight, "weight")
+    T, H = residual.shape
+    for i, p in enumerate(parts):
+        if p.dim() != 2 or p.shape[1] != H or p.shape[0] < token_offset + T or token_offset < 0:
+            raise ValueError(f"partials[{i}] must be [>= token_offset + T, H]")
+    kind = RS_PATTERNS[pattern]
+    residual_out = torch.empty_like(residual) if residual_out is None else residual_out
+    if "norm" in kind and norm_out is None:
+        norm_out = torch.empty_like(residual)
+    if kind != "norm" and quant_out is None:
+        quant_out = _fp8_out(residual)
+    if kind == "block" and scale_out is None:
+        scale_out = torch.empty(T, max(H // FP8_GROUP, 1), dtype=torch.float32,
+                                device=residual.device)
+    if kind.startswith("static"):
+        if scale_factor is None:
+            raise ValueError(f"pattern {pattern} needs scale_factor")
+        if not isinstance(scale_factor, torch.Tensor):
+            scale_factor = torch.tensor([float(scale_factor)], dtype=torch.float32,
+                                        device=residual.device)
+        _need(scale_factor, "scale_factor", dtype=torch.float32)
+        if scale_factor.numel() != 1:
+            raise ValueError("scale_factor must hold one value")
+    else:
+        scale_factor = None
+    for name, t in (("add_in", add_in), ("residual_out", residual_out), ("norm_out", norm_out)):
+        if t is not None:
+            _need(t, name)
+            _shape(t, name, (T, H))
+    if quant_out is not None:
+        _need(quant_out, "quant_out", dtype=None)
+        _shape(quant_out, "quant_out", (T, H), itemsize=1)
+    if scale_out is not None:
+        _need(scale_out, "scale_out", dtype=torch.float32)
+        _shape(scale_out, "scale_out", (T, H // FP8_GROUP) if H % FP8_GROUP == 0
+               else tuple(scale_out.shape))
+    _shape(weight, "weight", (H,))
+    _same_device([("add_in", add_in), ("residual_out", residual_out), ("norm_out", norm_out),
+                  ("quant_out", quant_out), ("scale_out", scale_out),
+                  ("scale_factor", scale_factor)] +
+                 [(f"partials[{i}]", p) for i, p in enumerate(parts)], residual.device)
+    _check("fused_rs_epilogue", _lib.fused_rs_epilogue(
+        int(pattern), arr, len(parts), int(token_offset), _ptr(add_in), _ptr(residual),
+        _ptr(weight), T, H, float(eps), _ptr(scale_factor), _ptr(norm_out), _ptr(residual_out),
+        _ptr(quant_out), _ptr(scale_out), _stream(residual.device, stream)))
+    return {"residual": residual_out, "norm": norm_out, "codes": quant_out,
+            "scales": scale_out if kind == "block" else None}
+
+
 def _qkv_layout(qkv: torch.Tensor):
     if not isinstance(qkv, torch.Tensor) or not qkv.is_cuda or qkv.dtype != torch.bfloat16:
         raise TypeError("qkv must be a bf16 GPU tensor")
@@ -398,7 +467,7 @@ def e4m3_encode(x: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None
 
 __all__ = [
     "fused_add_rmsnorm", "fused_add_rmsnorm_quant_fp8", "fused_add_rmsnorm_quant_fp8_block",
-    "fused_add_rmsnorm_quant_fp8_static",
+    "fused_add_rmsnorm_quant_fp8_static", "fused_rs_epilogue",
     "qk_rmsnorm", "qk_rmsnorm_var", "sharded_rmsnorm", "sharded_rmsnorm_var", "e4m3_encode",
     "version", "library_path",
     "FusedNormError", "FusedNormUnsupported", "FusedNormLibraryMissing",

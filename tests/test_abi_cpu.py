@@ -47,7 +47,7 @@ def test_header_declares_the_entry_points():
             "fused_add_rmsnorm_quant_fp8_block", "qk_rmsnorm", "qk_rmsnorm_var",
             "fusednorm_e4m3_encode", "fusednorm_status_string", "fusednorm_last_error",
             "fusednorm_version", "sharded_rmsnorm", "sharded_rmsnorm_var",
-            "fused_add_rmsnorm_quant_fp8_static"} <= names
+            "fused_add_rmsnorm_quant_fp8_static", "fused_rs_epilogue"} <= names
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -256,3 +256,27 @@ def test_static_quant_validation(lib):
     # the scale may not sit inside an output
     assert fs(parts(2), 2, addr(1), addr(2), 4, 64, 1e-6, ctypes.c_void_p(A + 5 * MB * 64 + 64),
               None, addr(4), addr(5), None) == 2
+
+
+def test_rs_epilogue_validation(lib):
+    rs = lib.fused_rs_epilogue
+    sc = ctypes.cast(addr(6), ctypes.c_void_p)
+
+    def call(pattern, add=None, P=2, T=4, off=0, norm=None, q=None, scale=None, factor=None):
+        return rs(pattern, parts(P), P, off, add, addr(1), addr(2), T, 256, 1e-6, factor, norm,
+                  addr(4), q, scale, None)
+
+    for pattern in (0, 3, 5):
+        assert call(pattern) == 2 and "not implemented" in last(lib)
+    assert call(9) == 1 and call(-1) == 1
+    assert call(8) == 1 and "needs add_in" in last(lib)
+    assert call(1, add=addr(7)) == 1 and "takes no add_in" in last(lib)
+    assert call(7, add=addr(7), P=16) == 1 and "no room for add_in" in last(lib)
+    assert call(1, off=-1) == 1
+    assert call(2, q=addr(5), norm=addr(3), factor=sc) == 1          # 2 writes no norm_out
+    assert call(4, q=addr(5), factor=sc) == 1                        # 4 needs norm_out
+    assert call(2, q=addr(5)) == 1 and "scale_factor" in last(lib)
+    assert call(6, q=addr(5)) == 1 and "scale_out" in last(lib)
+    assert call(7, add=addr(4), q=addr(5), scale=sc) == 2            # add_in inside residual_out
+    assert "add_in" in last(lib)
+    assert call(8, add=addr(7), T=0) == 0

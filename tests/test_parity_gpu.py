@@ -525,3 +525,35 @@ def test_static_scale_quant(fn, T, H, P, scale, want_norm):
         compare_bf16(u16(norm), ref["norm"], what="norm_out")
     say(f"static s={scale} T={T} H={H} P={P}:",
         compare_e4m3(u8(q), ref["codes"], ref["near_tie"]))
+
+
+
+# ----------------------------------------------------------------------------- reduce-scatter epilogue
+
+@pytest.mark.parametrize("pattern", [1, 2, 4, 6, 7, 8])
+@pytest.mark.parametrize("N,T,off,H,P", [(64, 16, 0, 1024, 2), (64, 16, 48, 7168, 8),
+                                         (3000, 1100, 1900, 8192, 4), (40, 7, 13, 384, 15)])
+def test_rs_epilogue(fn, pattern, N, T, off, H, P):
+    if pattern in (7, 8) and P > 15:
+        pytest.skip("add_in needs P <= 15")
+    g = torch.Generator().manual_seed(pattern * 1000 + N + H)
+    parts = [(torch.randn(N, H, generator=g) * 0.5).to(torch.bfloat16) for _ in range(P)]
+    add = (torch.randn(T, H, generator=g) * 0.5).to(torch.bfloat16) if pattern in (7, 8) else None
+    res = torch.randn(T, H, generator=g).to(torch.bfloat16)
+    w = (1 + 0.1 * torch.randn(H, generator=g)).to(torch.bfloat16)
+    scale = 0.02 if pattern in (2, 4) else None
+    out = fn.fused_rs_epilogue(pattern, [p.to(DEV) for p in parts], off, res.to(DEV), w.to(DEV),
+                               EPS, add_in=None if add is None else add.to(DEV),
+                               scale_factor=scale)
+    torch.cuda.synchronize()
+    ref = oracle.rs_epilogue(pattern, [wl.bits(p) for p in parts], off,
+                             None if add is None else wl.bits(add), wl.bits(res), wl.bits(w), EPS,
+                             scale_factor=scale)
+    compare_bf16(u16(out["residual"]), ref["residual"], max_ulp=0, what="residual_out")
+    if ref.get("norm") is not None:
+        compare_bf16(u16(out["norm"]), ref["norm"], what="norm_out")
+    if ref.get("codes") is not None:
+        rep = compare_e4m3(u8(out["codes"]), ref["codes"], ref["near_tie"])
+        if ref.get("scales") is not None:
+            compare_scales(out["scales"].cpu().numpy(), ref["scales"])
+        say(f"rs pattern {pattern} N={N} T={T} off={off} H={H} P={P}:", rep)
