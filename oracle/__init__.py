@@ -70,6 +70,10 @@ def _load():
     lib.orc_fused_add_rmsnorm_static.argtypes = [
         ctypes.POINTER(vp), ctypes.c_int, vp, vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
         ctypes.c_float, vp, vp, vp, vp, vp, vp]
+    lib.orc_ag_dual_rmsnorm.restype = ctypes.c_int
+    lib.orc_ag_dual_rmsnorm.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                        ctypes.c_int64, vp, vp, ctypes.c_float, ctypes.c_float,
+                                        vp, vp, vp, vp, vp, vp, vp]
     lib.orc_sharded_means.restype = ctypes.c_int
     lib.orc_sharded_means.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, vp]
     lib.orc_sharded_rmsnorm.restype = ctypes.c_int
@@ -267,6 +271,38 @@ def rs_epilogue(pattern: int, partials: Sequence[np.ndarray], token_offset: int,
     raise ValueError(f"pattern {pattern} is not implemented")
 
 
+# ----------------------------------------------------------------------------- all-gather epilogue (MLA)
+
+def ag_dual_rmsnorm(rows: np.ndarray, q_rank: int, kv_rank: int, x_gamma: np.ndarray,
+                    y_gamma: np.ndarray, x_eps: float, y_eps: float, quant: bool = False,
+                    want_x: bool = True, want_pre: bool = False) -> dict:
+    """The all-gather epilogue for MLA (tokenspeed trtllm.py page, section
+    "AllGather fusion"): RMSNorm of the q_lora_rank and kv_lora_rank segments of
+    each gathered row with their own weights and eps; with quant, 1x128 e4m3 of
+    the normalised q part. Returns ``x`` (or None), ``y``, and with quant
+    ``codes``, ``scales`` [T, q_rank/128], ``near_tie``."""
+    rows, T, stride = _rows(rows, q_rank + kv_rank)
+    xg, yg = _c(x_gamma, np.uint16), _c(y_gamma, np.uint16)
+    x_out = np.empty((T, q_rank), np.uint16) if want_x else None
+    y_out = np.empty((T, kv_rank), np.uint16)
+    codes = np.empty((T, q_rank), np.uint8) if quant else None
+    scales = np.empty((T, q_rank // 128), np.float32) if quant else None
+    tie = np.empty((T, q_rank), np.uint8) if quant else None
+    yx = np.empty((T, q_rank), np.float64) if want_pre else None
+    yy = np.empty((T, kv_rank), np.float64) if want_pre else None
+    rc = _load().orc_ag_dual_rmsnorm(_ptr(rows), T, stride, q_rank, kv_rank, _ptr(xg), _ptr(yg),
+                                     float(x_eps), float(y_eps), _ptr(x_out), _ptr(y_out),
+                                     _ptr(codes), _ptr(scales), _ptr(tie), _ptr(yx), _ptr(yy))
+    if rc != 0:
+        raise RuntimeError(f"oracle ag_dual_rmsnorm failed with code {rc}")
+    out = {"x": x_out, "y": y_out}
+    if quant:
+        out.update(codes=codes, scales=scales, near_tie=tie.astype(bool))
+    if want_pre:
+        out.update(yx=yx, yy=yy)
+    return out
+
+
 # ----------------------------------------------------------------------------- QK norm
 
 def _qk_view(qkv: np.ndarray, q_size: int, kv_size: int):
@@ -371,6 +407,7 @@ def sharded_rmsnorm(x: np.ndarray, H: int, weight: np.ndarray, eps: float, tp_wo
 
 __all__ = [
     "max_threads", "bf16_decode", "bf16_encode", "e4m3_decode", "e4m3_encode",
-    "fused_add_rmsnorm", "fused_add_rmsnorm_static", "rs_epilogue", "qk_means", "qk_rmsnorm",
+    "fused_add_rmsnorm", "fused_add_rmsnorm_static", "rs_epilogue", "ag_dual_rmsnorm",
+    "qk_means", "qk_rmsnorm",
     "sharded_means", "sharded_rmsnorm",
 ]

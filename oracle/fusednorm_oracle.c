@@ -469,3 +469,69 @@ int orc_fused_add_rmsnorm_static(const uint16_t* const* partials, int P, const u
     }
     return err;
 }
+
+/* ------------------------------------------------------------------------ */
+/* All-gather epilogue for MLA ([TS-TRTLLM] "AllGather fusion":             */
+/* trtllm_allgather_fusion, patterns kAllGatherfusedRMS and                  */
+/* kAllGatherfusedRMSFP8BlockWiseQuant). Each gathered row holds the         */
+/* q_lora_rank segment x, then the kv_lora_rank segment y, then the rope part */
+/* (never read). Two RMSNorms with their own weight and eps:                 */
+/*   x_out = bf16(x * rsqrt(mean(x^2) + x_eps) * x_gamma)                     */
+/*   y_out = bf16(y * rsqrt(mean(y^2) + y_eps) * y_gamma)                     */
+/* and, when codes != NULL, 1x128 e4m3 of the fp64 normalised x with one     */
+/* scale per group (scales [T, q_lora_rank/128]), as in the block variant of */
+/* the fused epilogue. x_out may be NULL; y_out may not.                     */
+/* ------------------------------------------------------------------------ */
+int orc_ag_dual_rmsnorm(const uint16_t* rows, int64_t T, int64_t row_stride, int64_t q_rank,
+                        int64_t kv_rank, const uint16_t* x_gamma, const uint16_t* y_gamma,
+                        float x_eps, float y_eps, uint16_t* x_out, uint16_t* y_out,
+                        uint8_t* codes, float* scales, uint8_t* near_tie, double* yx,
+                        double* yy) {
+    if (!rows || !x_gamma || !y_gamma || !y_out || T < 0 || q_rank <= 0 || kv_rank <= 0 ||
+        row_stride < q_rank + kv_rank)
+        return ORC_ERR_ARG;
+    if (codes && (!scales || q_rank % 128 != 0)) return ORC_ERR_ARG;
+    const int64_t groups = q_rank / 128;
+    int err = ORC_OK;
+#pragma omp parallel
+    {
+        double* vx = (double*)malloc((size_t)q_rank * sizeof(double));
+        if (!vx) {
+#pragma omp atomic write
+            err = ORC_ERR_NOMEM;
+        }
+#pragma omp for schedule(static)
+        for (int64_t t = 0; t < T; ++t) {
+            if (!vx) continue;
+            const uint16_t* row = rows + t * row_stride;
+            double sx = 0.0, sy = 0.0;
+            for (int64_t j = 0; j < q_rank; ++j) {
+                double v = orc_bf16_decode(row[j]);
+                sx += v * v;
+            }
+            for (int64_t j = 0; j < kv_rank; ++j) {
+                double v = orc_bf16_decode(row[q_rank + j]);
+                sy += v * v;
+            }
+            double inv_x = 1.0 / sqrt(sx / (double)q_rank + (double)x_eps);
+            double inv_y = 1.0 / sqrt(sy / (double)kv_rank + (double)y_eps);
+            for (int64_t j = 0; j < q_rank; ++j) {
+                vx[j] = orc_bf16_decode(row[j]) * inv_x * orc_bf16_decode(x_gamma[j]);
+                if (x_out) x_out[t * q_rank + j] = orc_bf16_encode(vx[j]);
+                if (yx) yx[t * q_rank + j] = vx[j];
+            }
+            for (int64_t j = 0; j < kv_rank; ++j) {
+                double v = orc_bf16_decode(row[q_rank + j]) * inv_y * orc_bf16_decode(y_gamma[j]);
+                y_out[t * kv_rank + j] = orc_bf16_encode(v);
+                if (yy) yy[t * kv_rank + j] = v;
+            }
+            if (codes)
+                for (int64_t g = 0; g < groups; ++g)
+                    orc_quant_block(vx + g * 128, 128, codes + t * q_rank + g * 128,
+                                    near_tie ? near_tie + t * q_rank + g * 128 : NULL,
+                                    scales + t * groups + g, NULL);
+        }
+        free(vx);
+    }
+    return err;
+}

@@ -19,7 +19,7 @@ from oracle import _build
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PIN_FILES = ["tests/test_oracle_codecs.py", "tests/test_oracle_norm.py",
              "tests/test_oracle_quant.py", "tests/test_oracle_qk.py", "tests/test_oracle_sharded.py",
-             "tests/test_oracle_static.py"]
+             "tests/test_oracle_static.py", "tests/test_oracle_ag.py"]
 
 # (name, text in the source, replacement)
 MUTANTS = [
@@ -83,6 +83,12 @@ MUTANTS = [
     ("static codes from bf16(y)",
      "codes[off + j] = orc_e4m3_encode(r);",
      "codes[off + j] = orc_e4m3_encode(orc_bf16_decode(orc_bf16_encode(y)) / s);"),
+    ("MLA y segment takes the x eps",
+     "double inv_y = 1.0 / sqrt(sy / (double)kv_rank + (double)y_eps);",
+     "double inv_y = 1.0 / sqrt(sy / (double)kv_rank + (double)x_eps);"),
+    ("MLA y segment reads the rope part",
+     "double v = orc_bf16_decode(row[q_rank + j]);\n                sy += v * v;",
+     "double v = orc_bf16_decode(row[row_stride - kv_rank + j]);\n                sy += v * v;"),
     ("sharded norm ignores tp_world",
      "double inv = 1.0 / sqrt(var / (double)tp_world + (double)eps);",
      "double inv = 1.0 / sqrt(var + (double)eps);"),
