@@ -185,6 +185,39 @@ int fused_rs_epilogue(int pattern, const void* const* partials, int P, int64_t t
                       void* residual_out, void* quant_out, float* scale_out, void* stream);
 
 /*
+ * ag_dual_rmsnorm -- the epilogue of the all-gather fusion for MLA on the
+ * gathered rows ([TS-TRTLLM] "AllGather fusion": trtllm_allgather_fusion with
+ * AllGatherFusionPattern 1 kAllGatherfusedRMS and 2
+ * kAllGatherfusedRMSFP8BlockWiseQuant; the gather itself is not part of this
+ * library). Token t's row starts at rows + t * row_stride and holds x
+ * (q_lora_rank elements), then y (kv_lora_rank), then the rope part (never read
+ * or written). Per token, in fp32:
+ *   x_norm_out[t,:] = bf16( x * rsqrt(mean(x^2) + x_eps) * x_gamma )
+ *   y_norm_out[t,:] = bf16( y * rsqrt(mean(y^2) + y_eps) * y_gamma )
+ * and, for pattern 2, the normalised x (before rounding to bf16) in 1x128 FP8
+ * groups as fused_add_rmsnorm_quant_fp8_block: for each group g of 128,
+ *   scale_out[t,g] = max|x_norm| / 448,
+ *   quant_out[t,j] = e4m3( x_norm[j] / scale_out[t,g] )   (zero group: codes 0)
+ *
+ *   pattern       1: x_norm_out and y_norm_out; quant_out, scale_out NULL
+ *                 2: y_norm_out, quant_out, scale_out; x_norm_out optional (NULL: not written)
+ *                 0 (the bare all-gather) returns FUSEDNORM_ERR_UNSUPPORTED
+ *   rows          bf16, 16-B aligned; row_stride (elements) a multiple of 8 and
+ *                 >= q_lora_rank + kv_lora_rank
+ *   q_lora_rank   multiple of 8 (of 128 for pattern 2); kv_lora_rank multiple of
+ *                 8; their sum <= 16384
+ *   x_gamma       bf16 [q_lora_rank];  y_gamma bf16 [kv_lora_rank]; 16-B aligned
+ *   x_eps, y_eps  >= 0
+ *   x_norm_out    bf16 [T, q_lora_rank];  y_norm_out bf16 [T, kv_lora_rank]
+ *   quant_out     e4m3 [T, q_lora_rank], 8-B aligned
+ *   scale_out     fp32 [T, q_lora_rank / 128], 4-B aligned
+ */
+int ag_dual_rmsnorm(int pattern, const void* rows, int64_t T, int64_t row_stride,
+                    int64_t q_lora_rank, int64_t kv_lora_rank, const void* x_gamma,
+                    const void* y_gamma, float x_eps, float y_eps, void* x_norm_out,
+                    void* y_norm_out, void* quant_out, float* scale_out, void* stream);
+
+/*
  * qk_rmsnorm -- the MiniMax QK RMSNorm under tensor parallelism ([VLLM-QK]
  * _minimax_qk_norm_tp_eager and _minimax_rms_apply_kernel; [TS-TRTLLM]
  * minimax_allreduce_rms_qk for the contiguous outputs).

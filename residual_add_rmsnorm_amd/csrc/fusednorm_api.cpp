@@ -277,6 +277,7 @@ int qk_common(const void* qkv, int64_t T, int64_t row_stride, int64_t q_size, in
     a.kv_size = (float)kv_size;
     a.tp_world = (float)tp_world;
     a.eps = eps;
+    a.eps_k = eps;
     if (!stats) mode = var_in ? fusednorm::kQkSupplied : fusednorm::kQkLocal;
     (void)hipGetLastError();
     int cus = 0;
@@ -351,6 +352,7 @@ int sharded_common(const void* x, int64_t T, int64_t row_stride, int64_t H, cons
     a.kv_size = 1.0f;
     a.tp_world = (float)tp_world;
     a.eps = eps;
+    a.eps_k = eps;
     if (!stats) mode = var_in ? fusednorm::kQkSupplied : fusednorm::kQkLocal;
     (void)hipGetLastError();
     int cus = 0;
@@ -358,6 +360,94 @@ int sharded_common(const void* x, int64_t T, int64_t row_stride, int64_t H, cons
     const fusednorm::LaunchShape shape = fusednorm::pick_qk_shape(a.nq, T, cus);
     if (shape.vpt == 0) return fail(FUSEDNORM_ERR_UNSUPPORTED, "no launch shape covers H");
     return hip_status(fusednorm::launch_qk(a, mode, T, shape, (hipStream_t)stream), "kernel launch");
+}
+
+int ag_common(int pattern, const void* rows, int64_t T, int64_t row_stride, int64_t q_rank,
+              int64_t kv_rank, const void* x_gamma, const void* y_gamma, float x_eps, float y_eps,
+              void* x_out, void* y_out, void* quant_out, float* scale_out, void* stream) {
+    if (pattern == 0)
+        return fail(FUSEDNORM_ERR_UNSUPPORTED, "pattern 0 (a bare all-gather) is not implemented");
+    if (pattern != 1 && pattern != 2)
+        return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "pattern %d is not an all-gather pattern",
+                    pattern);
+    const bool quant = pattern == 2;
+    if (T < 0) return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "T = %lld < 0", (long long)T);
+    if (q_rank <= 0 || kv_rank <= 0)
+        return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "q_lora_rank and kv_lora_rank must be > 0");
+    if (row_stride <= 0) return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "row_stride must be > 0");
+    if (int s = check_eps(x_eps)) return s;
+    if (int s = check_eps(y_eps)) return s;
+    if (q_rank % 8 || kv_rank % 8 || row_stride % 8)
+        return fail(FUSEDNORM_ERR_UNSUPPORTED,
+                    "q_lora_rank, kv_lora_rank and row_stride must be multiples of 8");
+    if (quant && q_rank % FUSEDNORM_FP8_GROUP)
+        return fail(FUSEDNORM_ERR_UNSUPPORTED, "q_lora_rank must be a multiple of %d",
+                    FUSEDNORM_FP8_GROUP);
+    if (row_stride < q_rank + kv_rank)
+        return fail(FUSEDNORM_ERR_UNSUPPORTED, "row_stride %lld < q_lora_rank + kv_lora_rank",
+                    (long long)row_stride);
+    if (q_rank + kv_rank > FUSEDNORM_MAX_HIDDEN)
+        return fail(FUSEDNORM_ERR_UNSUPPORTED, "q_lora_rank + kv_lora_rank above %d",
+                    FUSEDNORM_MAX_HIDDEN);
+    if (T > 0x7FFFFFFF) return fail(FUSEDNORM_ERR_UNSUPPORTED, "T above 2^31 - 1");
+    if (T == 0) return ok();  // nothing to read or write: buffers are not examined
+    if (!rows) return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "rows is NULL");
+    if (!x_gamma || !y_gamma)
+        return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "x_gamma / y_gamma is NULL");
+    if (!y_out) return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "y_norm_out is NULL");
+    if (quant) {
+        if (!quant_out || !scale_out)
+            return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "pattern 2 needs quant_out and scale_out");
+    } else {
+        if (!x_out) return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "x_norm_out is NULL");
+        if (quant_out || scale_out)
+            return fail(FUSEDNORM_ERR_INVALID_ARGUMENT, "pattern 1 writes no quant_out / scale_out");
+    }
+    if (!aligned(rows, 16) || !aligned(x_gamma, 16) || !aligned(y_gamma, 16) ||
+        !aligned(y_out, 16) || (x_out && !aligned(x_out, 16)))
+        return fail(FUSEDNORM_ERR_UNSUPPORTED, "rows, gammas and outputs must be 16-byte aligned");
+    if (quant && (!aligned(quant_out, 8) || !aligned(scale_out, 4)))
+        return fail(FUSEDNORM_ERR_UNSUPPORTED, "quant_out / scale_out misaligned");
+    const int64_t groups = q_rank / FUSEDNORM_FP8_GROUP;
+    Span in[3] = {span(rows, ((T - 1) * row_stride + q_rank + kv_rank) * 2, "rows"),
+                  span(x_gamma, q_rank * 2, "x_gamma"), span(y_gamma, kv_rank * 2, "y_gamma")};
+    Span out[4];
+    int n_out = 0;
+    out[n_out++] = span(y_out, T * kv_rank * 2, "y_norm_out");
+    if (x_out) out[n_out++] = span(x_out, T * q_rank * 2, "x_norm_out");
+    if (quant) {
+        out[n_out++] = span(quant_out, T * q_rank, "quant_out");
+        out[n_out++] = span(scale_out, T * groups * 4, "scale_out");
+    }
+    if (int s = check_overlaps(in, 3, out, n_out, -1, -1)) return s;
+
+    fusednorm::QkArgs a{};
+    a.qkv = static_cast<const uint16_t*>(rows);
+    a.row_stride = row_stride;
+    a.wq = static_cast<const u32x4*>(x_gamma);
+    a.wk = static_cast<const u32x4*>(y_gamma);
+    a.q_out = static_cast<u32x4*>(x_out);
+    a.k_out = static_cast<u32x4*>(y_out);
+    a.quant_out = static_cast<u32x2*>(quant_out);
+    a.scale_out = scale_out;
+    a.segments = 2;
+    a.nq = (int)(q_rank / 8);
+    a.nk = (int)(kv_rank / 8);
+    a.groups = (int)groups;
+    a.q_size = (float)q_rank;
+    a.kv_size = (float)kv_rank;
+    a.tp_world = 1.0f;
+    a.eps = x_eps;
+    a.eps_k = y_eps;
+    (void)hipGetLastError();
+    int cus = 0;
+    if (hipError_t e = fusednorm::device_cus(&cus)) return hip_status(e, "device query");
+    const fusednorm::LaunchShape shape = fusednorm::pick_qk_shape(a.nq + a.nk, T, cus);
+    if (shape.vpt == 0)
+        return fail(FUSEDNORM_ERR_UNSUPPORTED, "no launch shape covers q_lora_rank + kv_lora_rank");
+    return hip_status(fusednorm::launch_qk(a, quant ? fusednorm::kQkQuant : fusednorm::kQkLocal, T,
+                                           shape, (hipStream_t)stream),
+                      "kernel launch");
 }
 
 }  // namespace
@@ -455,6 +545,14 @@ int sharded_rmsnorm_var(const void* x, int64_t T, int64_t row_stride, int64_t H,
                         void* stream) {
     return sharded_common(x, T, row_stride, H, nullptr, 0.0f, 1, nullptr, nullptr, var_out, stream,
                           fusednorm::kQkStats);
+}
+
+int ag_dual_rmsnorm(int pattern, const void* rows, int64_t T, int64_t row_stride,
+                    int64_t q_lora_rank, int64_t kv_lora_rank, const void* x_gamma,
+                    const void* y_gamma, float x_eps, float y_eps, void* x_norm_out,
+                    void* y_norm_out, void* quant_out, float* scale_out, void* stream) {
+    return ag_common(pattern, rows, T, row_stride, q_lora_rank, kv_lora_rank, x_gamma, y_gamma,
+                     x_eps, y_eps, x_norm_out, y_norm_out, quant_out, scale_out, stream);
 }
 
 int fusednorm_e4m3_encode(const float* in, void* out, int64_t n, void* stream) {

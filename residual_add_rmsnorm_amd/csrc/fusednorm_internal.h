@@ -30,7 +30,8 @@ constexpr __host__ __device__ int max_threads_for(int vpt, int ch) {
 }
 
 enum EpilogueMode { kModeNorm = 0, kModeQuantToken = 1, kModeQuantBlock = 2, kModeQuantStatic = 3 };
-enum QkMode { kQkLocal = 0, kQkSupplied = 1, kQkStats = 2 };
+// kQkQuant: local means, plus 1x128 e4m3 of the normalised segment 1.
+enum QkMode { kQkLocal = 0, kQkSupplied = 1, kQkStats = 2, kQkQuant = 3 };
 
 struct EpilogueArgs {
     const u32x4* partials[kMaxPartials];  // P row-major bf16 [T, H]
@@ -49,15 +50,18 @@ struct EpilogueArgs {
     float eps;
 };
 
-// The QK norm and its one-segment form (sharded-hidden RMSNorm): each row holds
-// segment 1 (q, nq vectors) then, when segments == 2, segment 2 (k, nk vectors).
+// The QK norm, its one-segment form (sharded-hidden RMSNorm) and the MLA
+// all-gather epilogue: each row holds segment 1 (q, nq vectors) then, when
+// segments == 2, segment 2 (k, nk vectors); anything after them is not read.
 struct QkArgs {
     const uint16_t* qkv;                  // bf16 rows
     int64_t row_stride;                   // elements
     const u32x4* wq;                      // bf16 [q_size]
     const u32x4* wk;                      // bf16 [kv_size] (segments == 2)
-    u32x4* q_out;                         // bf16 [T, q_size]
+    u32x4* q_out;                         // bf16 [T, q_size] (may be null in kQkQuant)
     u32x4* k_out;                         // bf16 [T, kv_size] (segments == 2)
+    u32x2* quant_out;                     // e4m3 [T, q_size] (kQkQuant)
+    float* scale_out;                     // fp32 [T, q_size / 128] (kQkQuant)
     const float* var_in;                  // fp32 [T, segments] (supplied mode)
     float* var_out;                       // fp32 [T, segments] (statistics mode)
     int segments;                         // 1 or 2
@@ -65,8 +69,10 @@ struct QkArgs {
     int nk;                               // kv_size / 8 (0 when segments == 1)
     float q_size;
     float kv_size;                        // 1 when segments == 1 (unused)
+    int groups;                           // q_size / 128 (kQkQuant)
     float tp_world;
-    float eps;
+    float eps;                            // segment 1
+    float eps_k;                          // segment 2
 };
 
 struct LaunchShape {

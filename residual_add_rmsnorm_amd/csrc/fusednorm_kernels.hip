@@ -513,11 +513,15 @@ __global__ void __launch_bounds__(max_threads_for(VPT)) qk_norm_kernel(QkArgs a,
             }
         } else {
             const float inv_q = rsqrtf(var_q / a.tp_world + a.eps);
-            const float inv_k = rsqrtf(var_k / a.tp_world + a.eps);
-            const Row out_q = make_row(a.q_out + t * a.nq, (uint32_t)a.nq * 16u);
-            // one segment: the k resource covers zero bytes, so every k store is dropped
+            const float inv_k = rsqrtf(var_k / a.tp_world + a.eps_k);
+            // a null q_out (quantised q only) and the k output of one segment
+            // get resources of zero bytes: every store to them is dropped
+            const Row out_q = a.q_out ? make_row(a.q_out + t * a.nq, (uint32_t)a.nq * 16u)
+                                      : make_row(a.k_out, 0u);
             const Row out_k = seg == 2 ? make_row(a.k_out + t * a.nk, (uint32_t)a.nk * 16u)
                                        : make_row(a.q_out, 0u);
+            const Row out_c = MODE == kQkQuant ? make_row(a.quant_out + t * a.nq, (uint32_t)a.nq * 8u)
+                                               : out_k;
 #pragma unroll
             for (int s = 0; s < VPT; ++s) {
                 const float inv = is_q[s] ? inv_q : inv_k;
@@ -531,6 +535,29 @@ __global__ void __launch_bounds__(max_threads_for(VPT)) qk_norm_kernel(QkArgs a,
                 // check drops the store that does not apply
                 store16(out_q, off[s], pack_bf16x8(y));
                 store16(out_k, off[s] - (uint32_t)a.nq * 16u, pack_bf16x8(y));
+                if (MODE == kQkQuant) {
+                    // A 1x128 group is the 16 lanes of one DPP row in one slot;
+                    // q_size is a multiple of 128, so no group reaches into k.
+                    // As in the fused epilogue the codes come from x*w, which
+                    // the rsqrt multiplies away.
+                    float xw[8], r[8];
+                    float gmax = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        xw[e] = f[e] * w[e];
+                        gmax = fmaxf(gmax, fabsf(xw[e]));
+                    }
+                    gmax = row16_reduce(gmax, Max{});
+                    const QuantScale q = quant_scale(gmax);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) r[e] = (xw[e] * q.pre) * q.qmul;
+                    u32x2 codes = pack_e4m3x8(r);
+                    if (q.qmul == 0.0f) codes = u32x2{0u, 0u};  // all-zero group: +0 codes
+                    store8(out_c, off[s] / 2u, codes);       // k vectors: past the end, dropped
+                    const int i = s * nthr + tid;
+                    if (is_q[s] && (tid & 15) == 0)
+                        a.scale_out[t * a.groups + i / 16] = (gmax * inv_q) / 448.0f;
+                }
             }
         }
         if (!more) break;
@@ -653,7 +680,9 @@ hipError_t launch_qk_vpt(const QkArgs& a, QkMode mode, int64_t T, int threads, h
         case kQkLocal: return launch_persistent(qk_norm_kernel<VPT, kQkLocal>, a, T, threads, stream);
         case kQkSupplied:
             return launch_persistent(qk_norm_kernel<VPT, kQkSupplied>, a, T, threads, stream);
-        default: return launch_persistent(qk_norm_kernel<VPT, kQkStats>, a, T, threads, stream);
+        case kQkStats:
+            return launch_persistent(qk_norm_kernel<VPT, kQkStats>, a, T, threads, stream);
+        default: return launch_persistent(qk_norm_kernel<VPT, kQkQuant>, a, T, threads, stream);
     }
 }
 

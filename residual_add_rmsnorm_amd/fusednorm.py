@@ -59,6 +59,7 @@ def _load() -> ctypes.CDLL:
                                                vp],
         "fused_rs_epilogue": [i32, vpp, i32, i64, vp, vp, vp, i64, i64, f32, vp, vp, vp, vp, vp,
                               vp],
+        "ag_dual_rmsnorm": [i32, vp, i64, i64, i64, i64, vp, vp, f32, f32, vp, vp, vp, vp, vp],
         "qk_rmsnorm": [vp, i64, i64, i64, i64, vp, vp, f32, i32, vp, vp, vp, vp],
         "qk_rmsnorm_var": [vp, i64, i64, i64, i64, vp, vp],
         "sharded_rmsnorm": [vp, i64, i64, i64, vp, f32, i32, vp, vp, vp],
@@ -417,6 +418,57 @@ def qk_rmsnorm_var(qkv: torch.Tensor, q_size: int, kv_size: int,
     return var_out
 
 
+def ag_dual_rmsnorm(rows: torch.Tensor, q_lora_rank: int, kv_lora_rank: int,
+                    x_gamma: torch.Tensor, y_gamma: torch.Tensor, x_eps: float = 1e-6,
+                    y_eps: float = 1e-6, quant: bool = False, want_x: bool = True,
+                    x_norm_out: Optional[torch.Tensor] = None,
+                    y_norm_out: Optional[torch.Tensor] = None,
+                    quant_out: Optional[torch.Tensor] = None,
+                    scale_out: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """The MLA all-gather epilogue on gathered rows [T, q_lora_rank |
+    kv_lora_rank | rope] (rows may be strided): pattern 1 (quant=False) returns
+    ``x`` [T, q_lora_rank] and ``y`` [T, kv_lora_rank] bf16; pattern 2
+    (quant=True) also ``codes`` (e4m3 [T, q_lora_rank]) and ``scales`` (fp32
+    [T, q_lora_rank/128]), with ``x`` only when want_x."""
+    T, row_stride = _qkv_layout(rows)
+    q, kv = int(q_lora_rank), int(kv_lora_rank)
+    _need(x_gamma, "x_gamma")
+    _need(y_gamma, "y_gamma")
+    if not quant:
+        want_x = True
+    if want_x and x_norm_out is None:
+        x_norm_out = torch.empty(T, q, dtype=rows.dtype, device=rows.device)
+    y_norm_out = torch.empty(T, kv, dtype=rows.dtype, device=rows.device) if y_norm_out is None \
+        else y_norm_out
+    if quant:
+        if quant_out is None:
+            quant_out = torch.empty(T, q, dtype=torch.float8_e4m3fn, device=rows.device)
+        if scale_out is None:
+            scale_out = torch.empty(T, max(q // 128, 1), dtype=torch.float32, device=rows.device)
+        _need(quant_out, "quant_out", dtype=None)
+        _need(scale_out, "scale_out", dtype=torch.float32)
+    for name, t in (("x_norm_out", x_norm_out), ("y_norm_out", y_norm_out)):
+        if t is not None:
+            _need(t, name)
+    tensors = [("x_gamma", x_gamma, (q,)), ("y_gamma", y_gamma, (kv,)),
+               ("x_norm_out", x_norm_out, (T, q)), ("y_norm_out", y_norm_out, (T, kv))]
+    if quant:
+        # a q_lora_rank that is no multiple of 128 is refused by the library
+        tensors += [("scale_out", scale_out, (T, q // 128) if q % 128 == 0 else scale_out.shape),
+                    ("quant_out", quant_out, (T, q))]
+        _shape(quant_out, "quant_out", (T, q), itemsize=1)
+    _check_qk_shapes(rows, q, kv, tensors)
+    _check("ag_dual_rmsnorm", _lib.ag_dual_rmsnorm(
+        2 if quant else 1, _ptr(rows), T, row_stride, q, kv, _ptr(x_gamma), _ptr(y_gamma),
+        float(x_eps), float(y_eps), _ptr(x_norm_out), _ptr(y_norm_out),
+        _ptr(quant_out if quant else None), _ptr(scale_out if quant else None),
+        _stream(rows.device, stream)))
+    out = {"x": x_norm_out, "y": y_norm_out}
+    if quant:
+        out.update(codes=quant_out, scales=scale_out)
+    return out
+
+
 def sharded_rmsnorm(x: torch.Tensor, weight: torch.Tensor, eps: float = 1e-6, tp_world: int = 1,
                     var_in: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                     H: Optional[int] = None, stream=None) -> torch.Tensor:
@@ -467,7 +519,7 @@ def e4m3_encode(x: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None
 
 __all__ = [
     "fused_add_rmsnorm", "fused_add_rmsnorm_quant_fp8", "fused_add_rmsnorm_quant_fp8_block",
-    "fused_add_rmsnorm_quant_fp8_static", "fused_rs_epilogue",
+    "fused_add_rmsnorm_quant_fp8_static", "fused_rs_epilogue", "ag_dual_rmsnorm",
     "qk_rmsnorm", "qk_rmsnorm_var", "sharded_rmsnorm", "sharded_rmsnorm_var", "e4m3_encode",
     "version", "library_path",
     "FusedNormError", "FusedNormUnsupported", "FusedNormLibraryMissing",

@@ -14,11 +14,15 @@ mask when the workload has outliers, then cast to bf16):
 QK workloads: qkv = randn(T, row) with its outlier mask; wq = 1 + 0.1 randn(q);
 wk = 1 + 0.1 randn(kv); then tp_world - 1 further shard rows drawn like qkv
 (the other ranks' local rows, used only to form the sum of shard means).
+The MLA all-gather workload draws like a QK workload: the gathered rows
+(q_lora_rank | kv_lora_rank | rope), then the x and y gammas.
 
 The shapes follow the pages' workloads: a 7168-wide decode step, 8192-wide
 prefill with per-token FP8, 7168-wide block-FP8 with 1x128 groups, and the
 MiniMax-M2 attention shard (global q 6144 / k 1024, from the tokenspeed
-``trtllm.py`` page, section "MiniMax QK fused AR + RMSNorm").
+``trtllm.py`` page, section "MiniMax QK fused AR + RMSNorm"), and MLA rows of
+q_lora_rank 1536 | kv_lora_rank 512 | rope 64 = 2112, the largest hidden width
+the same page's "AllGather fusion" section accepts.
 """
 from __future__ import annotations
 
@@ -32,7 +36,7 @@ import torch
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str                      # "norm", "quant_token", "quant_block", "qk"
+    kind: str                      # "norm", "quant_token", "quant_block", "qk", "mla"
     T: int
     H: int = 0                     # hidden width (fused epilogue)
     P: int = 0                     # number of partial buffers
@@ -46,7 +50,7 @@ class Workload:
     tp_world: int = 1              # QK mode B: shards folded into the rsqrt
     eps: float = 1e-6
     seed: int = 0
-    want_norm: bool = True         # FP8 kinds: also write bf16 norm_out
+    want_norm: bool = True         # FP8 kinds: also write bf16 norm_out (MLA: x_norm_out)
     description: str = ""
 
     def with_tokens(self, T: int) -> "Workload":
@@ -60,6 +64,12 @@ class Workload:
             write = (self.q_size + self.kv_size) * 2
             var = 8 if self.tp_world > 1 else 0
             return read + write + var
+        if self.kind == "mla":
+            read = (self.q_size + self.kv_size) * 2
+            write = self.kv_size * 2 + self.q_size + 4 * (self.q_size // self.group_size)
+            if self.want_norm:
+                write += self.q_size * 2
+            return read + write
         read = (self.P + 1) * self.H * 2
         write = self.H * 2                                   # residual_out
         if self.kind == "norm" or self.want_norm:
@@ -71,7 +81,7 @@ class Workload:
         return read + write
 
     def weight_bytes(self) -> int:
-        if self.kind == "qk":
+        if self.kind in ("qk", "mla"):
             return (self.q_size + self.kv_size) * 2
         return self.H * 2
 
@@ -103,6 +113,11 @@ WORKLOADS: Dict[str, Workload] = {
         "qk_sharded", "qk", T=4096, row_stride=8192, q_size=6144, kv_size=1024,
         outlier_frac=0.01, outlier_mult=50.0, tp_world=4,
         description="MiniMax QK RMSNorm T=4096, supplied sum of 4 shard means, tp_world=4"),
+    "mla_ag_fp8": Workload(
+        "mla_ag_fp8", "mla", T=8192, row_stride=2112, q_size=1536, kv_size=512,
+        outlier_frac=0.001, outlier_mult=64.0, want_norm=False,
+        description="MLA all-gather epilogue T=8192 rows of 1536 | 512 | 64: y bf16, "
+                    "x as 1x128 e4m3 + fp32 scales"),
 }
 
 
@@ -140,7 +155,7 @@ def make_inputs(w: Workload, T: Optional[int] = None, seed: Optional[int] = None
         w = w.with_tokens(T)
     gen = torch.Generator(device="cpu")
     gen.manual_seed(w.seed if seed is None else int(seed))
-    if w.kind == "qk":
+    if w.kind in ("qk", "mla"):
         qkv = _draw(gen, (w.T, w.row_stride), 1.0, w.outlier_frac, w.outlier_mult)
         wq = (1.0 + 0.1 * torch.randn(w.q_size, generator=gen)).to(torch.bfloat16)
         wk = (1.0 + 0.1 * torch.randn(w.kv_size, generator=gen)).to(torch.bfloat16)

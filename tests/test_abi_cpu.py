@@ -47,7 +47,7 @@ def test_header_declares_the_entry_points():
             "fused_add_rmsnorm_quant_fp8_block", "qk_rmsnorm", "qk_rmsnorm_var",
             "fusednorm_e4m3_encode", "fusednorm_status_string", "fusednorm_last_error",
             "fusednorm_version", "sharded_rmsnorm", "sharded_rmsnorm_var",
-            "fused_add_rmsnorm_quant_fp8_static", "fused_rs_epilogue"} <= names
+            "fused_add_rmsnorm_quant_fp8_static", "fused_rs_epilogue", "ag_dual_rmsnorm"} <= names
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -280,3 +280,35 @@ def test_rs_epilogue_validation(lib):
     assert call(7, add=addr(4), q=addr(5), scale=sc) == 2            # add_in inside residual_out
     assert "add_in" in last(lib)
     assert call(8, add=addr(7), T=0) == 0
+
+
+def test_ag_dual_validation(lib):
+    ag = lib.ag_dual_rmsnorm
+    sc = ctypes.cast(addr(6), ctypes.c_void_p)
+
+    def call(pattern=1, T=4, stride=336, q=256, kv=64, xe=1e-6, ye=1e-6, rows=None, x="d",
+             y="d", codes=None, scale=None):
+        x = addr(3) if x == "d" else x
+        y = addr(4) if y == "d" else y
+        return ag(pattern, rows or addr(1), T, stride, q, kv, addr(2), addr(7), xe, ye, x, y,
+                  codes, scale, None)
+
+    assert call(T=0) == 0 and call(2, T=0) == 0
+    assert call(0) == 2 and "not implemented" in last(lib)
+    assert call(3) == 1 and call(-1) == 1
+    assert call(q=0) == 1 and call(kv=0) == 1
+    assert call(T=-1) == 1
+    assert call(ye=-1.0) == 1 and call(xe=float("inf")) == 1
+    assert call(q=252) == 2
+    assert call(2, q=264, stride=336, codes=addr(5), scale=sc) == 2 and "128" in last(lib)
+    assert call(stride=312) == 2 and "row_stride" in last(lib)
+    assert call(q=16384, kv=8, stride=16392) == 2
+    assert call(x=None) == 1 and "x_norm_out" in last(lib)
+    assert call(y=None) == 1
+    assert call(codes=addr(5), scale=sc) == 1 and "pattern 1" in last(lib)
+    assert call(2, codes=addr(5)) == 1 and "scale_out" in last(lib)
+    assert call(2, scale=sc) == 1
+    assert call(rows=addr(1, 8)) == 2
+    assert call(2, x=None, codes=addr(5, 4), scale=sc) == 2
+    assert call(y=addr(1, 64)) == 2 and "overlaps" in last(lib)
+    assert call(2, x=None, codes=addr(4, 64), scale=sc) == 2 and "overlaps" in last(lib)

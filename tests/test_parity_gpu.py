@@ -557,3 +557,35 @@ def test_rs_epilogue(fn, pattern, N, T, off, H, P):
         if ref.get("scales") is not None:
             compare_scales(out["scales"].cpu().numpy(), ref["scales"])
         say(f"rs pattern {pattern} N={N} T={T} off={off} H={H} P={P}:", rep)
+
+
+# ----------------------------------------------------------------------------- MLA all-gather epilogue
+
+@pytest.mark.parametrize("T", [1, 37, 2500])
+@pytest.mark.parametrize("q,kv,stride", [(128, 8, 144), (256, 64, 336), (1536, 512, 2112),
+                                         (1536, 512, 2176), (3072, 1024, 4160)])
+@pytest.mark.parametrize("quant", [False, True])
+def test_ag_dual_rmsnorm(fn, T, q, kv, stride, quant):
+    g = torch.Generator().manual_seed(q + kv + stride + T)
+    rows = torch.randn(T, stride, generator=g).to(torch.bfloat16)
+    rows[:, q + kv:] = float("nan")                       # rope part and padding: never read
+    if T > 1:
+        rows[T // 2, :q + kv] = 0                         # an all-zero token: codes 0, scales 0
+        rows[T // 3, :128] = 0                            # an all-zero q group
+        rows[T // 4, 5] = 60.0                            # an outlier in one group
+    gx = (1 + 0.1 * torch.randn(q, generator=g)).to(torch.bfloat16)
+    gy = (1 + 0.1 * torch.randn(kv, generator=g)).to(torch.bfloat16)
+    xe, ye = 1e-6, 0.25                                  # the second eps is visible in y
+    out = fn.ag_dual_rmsnorm(rows.to(DEV), q, kv, gx.to(DEV), gy.to(DEV), xe, ye, quant=quant,
+                             want_x=not quant or T != 37)
+    torch.cuda.synchronize()
+    ref = oracle.ag_dual_rmsnorm(wl.bits(rows), q, kv, wl.bits(gx), wl.bits(gy), xe, ye,
+                                 quant=quant)
+    compare_bf16(u16(out["y"]), ref["y"], what="y_norm_out")
+    if out["x"] is not None:
+        compare_bf16(u16(out["x"]), ref["x"], what="x_norm_out")
+    if quant:
+        compare_scales(out["scales"].cpu().numpy(), ref["scales"])
+        say(f"ag q={q} kv={kv} stride={stride} T={T}:",
+            compare_e4m3(u8(out["codes"]), ref["codes"], ref["near_tie"]))
+
