@@ -17,6 +17,10 @@ Python). ``per_launch`` and ``roofline`` come from a separate eager pass of K
 steps in which every launch is bracketed by HIP events on its stream; the
 roofline is the dominant kernel's (the per-token FP8 epilogue).
 ``cpu_baseline`` times the CPU oracle on one full step of the same inputs.
+``next_rows`` times the further entry points (sharded-hidden RMSNorm post
+stage, static-scale FP8, reduce-scatter epilogue, MLA all-gather epilogue) one
+launch at a time, each right after a prefill launch that evicts the last-level
+cache, so every timed launch reads its inputs from HBM.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu-baseline]
 """
@@ -36,6 +40,8 @@ KERNEL_SRC = os.path.join(ROOT, "residual_add_rmsnorm_amd", "csrc", "fusednorm_k
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_fp8_token.json")
 STEP = ["prefill_fp8_token", "qk_local", "fp8_block", "qk_sharded"]
 DOMINANT = "prefill_fp8_token"
+# Entry points beyond the step, each timed alone on its own workload.
+NEXT = ["sharded_post", "static_fp8", "rs_fp8_block", "mla_ag_fp8"]
 
 
 def log(*a):
@@ -49,6 +55,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU oracle leg (for profiler runs)")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip timing the entry points beyond the step")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
     return ap.parse_args()
 
@@ -95,6 +103,26 @@ class Part:
             self.call = lambda: fn.qk_rmsnorm(self.qkv, w.q_size, w.kv_size, self.wq, self.wk,
                                               w.eps, tp_world=w.tp_world, var_in=self.var_in,
                                               q_out=self.q_out, k_out=self.k_out)
+        elif w.kind == "sharded":
+            self.x = self.cpu.qkv.to(dev)
+            self.weight = self.cpu.q_weight.to(dev)
+            self.out = torch.empty(w.T, w.q_size, dtype=torch.bfloat16, device=dev)
+            shards = [self.x] + [s.to(dev) for s in self.cpu.shards]
+            self.var_in = sum(fn.sharded_rmsnorm_var(s, H=w.q_size) for s in shards)
+            del shards
+            self.call = lambda: fn.sharded_rmsnorm(self.x, self.weight, w.eps, w.tp_world,
+                                                   self.var_in, out=self.out, H=w.q_size)
+        elif w.kind == "mla":
+            self.rows = self.cpu.qkv.to(dev)
+            self.gx, self.gy = self.cpu.q_weight.to(dev), self.cpu.k_weight.to(dev)
+            self.y = torch.empty(w.T, w.kv_size, dtype=torch.bfloat16, device=dev)
+            self.quant = torch.empty(w.T, w.q_size, dtype=torch.float8_e4m3fn, device=dev)
+            self.scale = torch.empty(w.T, w.q_size // w.group_size, dtype=torch.float32,
+                                     device=dev)
+            self.call = lambda: fn.ag_dual_rmsnorm(self.rows, w.q_size, w.kv_size, self.gx,
+                                                   self.gy, w.eps, w.eps, quant=True,
+                                                   want_x=False, y_norm_out=self.y,
+                                                   quant_out=self.quant, scale_out=self.scale)
         else:
             self.parts = [p.to(dev) for p in self.cpu.partials]
             self.res = self.cpu.residual.to(dev)
@@ -104,13 +132,25 @@ class Part:
             if w.kind == "quant_token":
                 self.scale = torch.empty(w.T, dtype=torch.float32, device=dev)
                 f = fn.fused_add_rmsnorm_quant_fp8
-            else:
+            elif w.kind in ("quant_block", "rs"):
                 self.scale = torch.empty(w.T, w.H // w.group_size, dtype=torch.float32,
                                          device=dev)
                 f = fn.fused_add_rmsnorm_quant_fp8_block
-            self.call = lambda: f(self.parts, self.res, self.weight, w.eps, norm_out=None,
-                                  residual_out=self.res_out, quant_out=self.quant,
-                                  scale_out=self.scale)
+            if w.kind == "quant_static":
+                self.factor = torch.tensor([w.static_scale], dtype=torch.float32, device=dev)
+                self.call = lambda: fn.fused_add_rmsnorm_quant_fp8_static(
+                    self.parts, self.res, self.weight, self.factor, w.eps, norm_out=None,
+                    residual_out=self.res_out, quant_out=self.quant)
+            elif w.kind == "rs":
+                self.add_in = self.cpu.add_in.to(dev)
+                self.call = lambda: fn.fused_rs_epilogue(
+                    w.pattern, self.parts, w.token_offset, self.res, self.weight, w.eps,
+                    add_in=self.add_in, residual_out=self.res_out, quant_out=self.quant,
+                    scale_out=self.scale)
+            else:
+                self.call = lambda: f(self.parts, self.res, self.weight, w.eps, norm_out=None,
+                                      residual_out=self.res_out, quant_out=self.quant,
+                                      scale_out=self.scale)
         self.bytes = w.algorithmic_bytes()
         log(f"[bench] {name}: {w.description}; {self.bytes / 1e6:.1f} MB per launch "
             f"(inputs drawn in {time.perf_counter() - t0:.1f} s)")
@@ -214,6 +254,33 @@ def latency_shapes(fn, wl, torch, dev, calls=50, reps=20):
         out[name] = {"T": w.T, "H": w.H, "P": w.P, "us_per_call": round(us, 2),
                      "GB/s": round(w.algorithmic_bytes() / us / 1e3, 1), "cache_resident": True}
         log(f"[bench] {name}: {us:.2f} us per call (graph replay, cache-resident)")
+    return out
+
+
+def next_rows(parts, flush, torch, K):
+    """Each further entry point timed alone: K launches, each preceded by an
+    untimed launch of `flush` (over 1 GB) so that its inputs are not in the
+    last-level cache, and bracketed by HIP events on the launch stream."""
+    out = {}
+    for p in parts:
+        for _ in range(2):
+            p.call()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(K)]
+        for s, e in ev:
+            flush.call()
+            s.record()
+            p.call()
+            e.record()
+        torch.cuda.synchronize()
+        us = sum(s.elapsed_time(e) for s, e in ev) / K * 1e3
+        gbs = p.bytes / us / 1e3
+        out[p.name] = {"workload": p.w.description, "us": round(us, 2), "GB/s": round(gbs, 1),
+                       "frac": round(gbs / HBM_PEAK_GBS, 4),
+                       "tokens/s": round(p.w.T / us * 1e6),
+                       "algorithmic_bytes_per_launch": p.bytes}
+        log(f"[bench] next {p.name}: {us:.1f} us, {gbs:.1f} GB/s "
+            f"({100 * gbs / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f})")
     return out
 
 
@@ -326,6 +393,11 @@ def main():
         "device_copy_GBs": device_copy(torch, dev),
         "latency_shapes": latency_shapes(fn, wl, torch, dev),
     }
+    if not args.no_next:
+        del g
+        extra = [Part(n, fn, wl, torch, dev) for n in NEXT]
+        result["next_rows"] = next_rows(extra, dom, torch, K)
+        del extra
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(parts)
     line = json.dumps(result)

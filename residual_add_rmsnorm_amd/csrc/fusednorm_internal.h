@@ -78,7 +78,9 @@ struct QkArgs {
 struct LaunchShape {
     int vpt;      // 16-byte vectors per lane
     int threads;  // workgroup size, a multiple of 64
-    int ch;       // fused epilogue: partial buffers loaded together (2, 4 or 8)
+    int ch;       // fused epilogue: partial buffers loaded together (2 or 4)
+    int per_cu;   // 0: one workgroup per token; k > 0: at most k resident
+                  // workgroups per CU, each looping over tokens
 };
 
 // Launch shape of the fused epilogue for T rows of nvec 16-byte vectors and P

@@ -8,11 +8,11 @@
 // and the vLLM minimax_rms_norm/rms_norm_tp page (_minimax_qk_var_kernel,
 // _minimax_rms_apply_kernel). How it is computed is designed for CDNA4:
 //
-//   * persistent workgroups: workgroup b handles tokens b, b + G, b + 2G, ...
-//     (G = at most two resident workgroups per CU), and issues the next
-//     token's loads as soon as the current token's sum is formed, so HBM
-//     requests stay in flight while a token is reduced, normalised and stored;
-//     the weight vector is loaded once per workgroup;
+//   * the grid: for rows of 32 KB of input and more per token, two resident
+//     workgroups per CU, each looping over tokens and issuing the next
+//     token's loads as soon as the current token's sum is formed; for smaller
+//     rows (and the QK family), one workgroup per token, the hardware
+//     dispatcher keeping every CU filled as workgroups finish;
 //   * a token's row is cut into 16-byte vectors (8 bf16); vector i belongs to
 //     lane i mod blockDim, slot i / blockDim, so every wave-wide access covers
 //     1 KiB of consecutive bytes, read and written through per-row buffer
@@ -320,10 +320,12 @@ __device__ __forceinline__ void sum_token(const EpilogueArgs& a, int n0, int64_t
     }
 }
 
-// One workgroup handles tokens blockIdx.x, blockIdx.x + gridDim.x, ... (the
-// grid holds as many workgroups as fit on the GPU at once). The next token's
-// loads are issued as soon as the current token's sum is formed, so they are
-// in flight while the current token is reduced, normalised and stored.
+// The fused epilogue. Workgroup b handles tokens b, b + gridDim.x, ... The
+// first chunk of partial buffers and the residual are loaded together, any
+// further partials two buffers at a time; when the grid is smaller than T, the
+// next token's first loads are issued as soon as the current token's sum is
+// formed, so they are in flight while the current token is reduced,
+// normalised and stored.
 template <int VPT, int MODE, int CH>
 __global__ void __launch_bounds__(max_threads_for(VPT, CH))
 fused_epilogue_kernel(EpilogueArgs a, int64_t T) {
@@ -433,9 +435,8 @@ fused_epilogue_kernel(EpilogueArgs a, int64_t T) {
 
 // ---------------------------------------------------------------- QK RMSNorm
 
-// One workgroup per token at a time, looping over tokens blockIdx.x,
-// blockIdx.x + gridDim.x, ... like the fused epilogue; the next token's row is
-// loaded while the current one is reduced and written.
+// The QK norm family. Workgroup b handles row b (and b + gridDim.x, ... when
+// the grid is smaller than T).
 template <int VPT, int MODE>
 __global__ void __launch_bounds__(max_threads_for(VPT)) qk_norm_kernel(QkArgs a, int64_t T) {
     const int tid = threadIdx.x;
@@ -455,36 +456,20 @@ __global__ void __launch_bounds__(max_threads_for(VPT)) qk_norm_kernel(QkArgs a,
         wv[s] = !valid[s] ? zero4() : is_q[s] ? a.wq[i] : a.wk[i - a.nq];
     }
 
-    int64_t t = blockIdx.x;  // the host launches at most T workgroups
-    u32x4 next[VPT];
-    float2 next_var = make_float2(0.0f, 0.0f);
     const int seg = a.segments;
     const uint32_t qk_bytes = (uint32_t)nv * 16u;  // q and k; v is never read
-    {
-        const Row src = make_row(a.qkv + t * a.row_stride, qk_bytes);
+    int parity = 0;
+    for (int64_t t = blockIdx.x; t < T; t += gridDim.x, parity ^= 1) {
+        u32x4 raw[VPT];  // lanes past the row read zeros
+        {
+            const Row src = make_row(a.qkv + t * a.row_stride, qk_bytes);
 #pragma unroll
-        for (int s = 0; s < VPT; ++s) next[s] = load16(src, off[s]);
-    }
-    if (MODE == kQkSupplied) {
-        next_var.x = a.var_in[t * seg];
-        if (seg == 2) next_var.y = a.var_in[t * seg + 1];
-    }
-
-    for (int parity = 0;; parity ^= 1) {
-        u32x4 raw[VPT];
-#pragma unroll
-        for (int s = 0; s < VPT; ++s) raw[s] = next[s];  // lanes past the row hold zeros
-        const float2 var_in = next_var;
-        const int64_t t_next = t + gridDim.x;
-        const bool more = t_next < T;
-        if (more) {
-            const Row src = make_row(a.qkv + t_next * a.row_stride, qk_bytes);
-#pragma unroll
-            for (int s = 0; s < VPT; ++s) next[s] = load16(src, off[s]);
-            if (MODE == kQkSupplied) {
-                next_var.x = a.var_in[t_next * seg];
-                if (seg == 2) next_var.y = a.var_in[t_next * seg + 1];
-            }
+            for (int s = 0; s < VPT; ++s) raw[s] = load16(src, off[s]);
+        }
+        float2 var_in = make_float2(0.0f, 0.0f);
+        if (MODE == kQkSupplied) {
+            var_in.x = a.var_in[t * seg];
+            if (seg == 2) var_in.y = a.var_in[t * seg + 1];
         }
 
         float var_q, var_k;
@@ -560,8 +545,6 @@ __global__ void __launch_bounds__(max_threads_for(VPT)) qk_norm_kernel(QkArgs a,
                 }
             }
         }
-        if (!more) break;
-        t = t_next;
     }
 }
 
@@ -585,7 +568,8 @@ __global__ void __launch_bounds__(256) e4m3_encode_kernel(const float* in, uint8
 // ---------------------------------------------------------------- dispatch
 
 // Compute units of the current device, and workgroups of `kernel` that fit
-// on one CU at once; cached per device, kernel and workgroup size.
+// on one CU at once (0 when no kernel is given); cached per device, kernel
+// and workgroup size.
 struct Residency {
     int cus;
     int per_cu;
@@ -615,61 +599,67 @@ hipError_t residency(const void* kernel, int threads, Residency* out) {
     if (kernel) {
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&r.per_cu, kernel, threads, 0);
         if (e != hipSuccess) return e;
+        if (r.per_cu < 1) r.per_cu = 1;
     }
     e = hipDeviceGetAttribute(&r.cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
     if (r.cus < 1) r.cus = 1;
-    if (r.per_cu < 1) r.per_cu = 1;
     std::lock_guard<std::mutex> lock(mu);
     cache.push_back(Entry{dev, kernel, threads, r});
     *out = r;
     return hipSuccess;
 }
 
-// Launches one workgroup per token slot: at most two resident workgroups per
-// CU (more made no difference or ran slower on MI355X, whose 256 MB last-level
-// cache and HBM3E queues are already full with two), and never more than T.
+// per_cu == 0: one workgroup per token (past kMaxGrid tokens, each workgroup
+// also takes tokens blockIdx.x + gridDim.x, ...; a dispatch counts its
+// work-items in 32 bits). per_cu > 0: at most per_cu resident workgroups per
+// CU, each looping over tokens. Never more workgroups than tokens.
+constexpr int64_t kMaxGrid = 1 << 20;
+
 template <typename Args>
-hipError_t launch_persistent(void (*kernel)(Args, int64_t), const Args& a, int64_t T, int threads,
-                             hipStream_t stream) {
-    Residency r{};
-    hipError_t e = residency(reinterpret_cast<const void*>(kernel), threads, &r);
-    if (e != hipSuccess) return e;
-    const int64_t resident = (int64_t)r.cus * (r.per_cu < 2 ? r.per_cu : 2);
-    const int64_t grid = T < resident ? T : resident;
+hipError_t launch_tokens(void (*kernel)(Args, int64_t), const Args& a, int64_t T, int threads,
+                         int per_cu, hipStream_t stream) {
+    int64_t cap = kMaxGrid;
+    if (per_cu > 0) {
+        Residency r{};
+        hipError_t e = residency(reinterpret_cast<const void*>(kernel), threads, &r);
+        if (e != hipSuccess) return e;
+        cap = (int64_t)r.cus * (r.per_cu < per_cu ? r.per_cu : per_cu);
+    }
+    const int64_t grid = T < cap ? T : cap;
     kernel<<<dim3((unsigned)grid), dim3((unsigned)threads), 0, stream>>>(a, T);
     return hipGetLastError();
 }
 
 template <int VPT, int CH>
 hipError_t launch_epilogue_ch(const EpilogueArgs& a, EpilogueMode mode, int64_t T, int threads,
-                              hipStream_t stream) {
+                              int per_cu, hipStream_t stream) {
     if constexpr (VPT * CH > kMaxLoadsPerLane) {
         return hipErrorInvalidValue;  // never picked: see pick_epilogue_shape
     } else {
         switch (mode) {
             case kModeNorm:
-                return launch_persistent(fused_epilogue_kernel<VPT, kModeNorm, CH>, a, T, threads,
-                                         stream);
+                return launch_tokens(fused_epilogue_kernel<VPT, kModeNorm, CH>, a, T, threads,
+                                     per_cu, stream);
             case kModeQuantToken:
-                return launch_persistent(fused_epilogue_kernel<VPT, kModeQuantToken, CH>, a, T,
-                                         threads, stream);
+                return launch_tokens(fused_epilogue_kernel<VPT, kModeQuantToken, CH>, a, T,
+                                     threads, per_cu, stream);
             case kModeQuantBlock:
-                return launch_persistent(fused_epilogue_kernel<VPT, kModeQuantBlock, CH>, a, T,
-                                         threads, stream);
+                return launch_tokens(fused_epilogue_kernel<VPT, kModeQuantBlock, CH>, a, T,
+                                     threads, per_cu, stream);
             default:
-                return launch_persistent(fused_epilogue_kernel<VPT, kModeQuantStatic, CH>, a, T,
-                                         threads, stream);
+                return launch_tokens(fused_epilogue_kernel<VPT, kModeQuantStatic, CH>, a, T,
+                                     threads, per_cu, stream);
         }
     }
 }
 
 template <int VPT>
 hipError_t launch_epilogue_vpt(const EpilogueArgs& a, EpilogueMode mode, int64_t T, int threads,
-                               int ch, hipStream_t stream) {
+                               int ch, int per_cu, hipStream_t stream) {
     switch (ch) {
-        case 2: return launch_epilogue_ch<VPT, 2>(a, mode, T, threads, stream);
-        case 4: return launch_epilogue_ch<VPT, 4>(a, mode, T, threads, stream);
+        case 2: return launch_epilogue_ch<VPT, 2>(a, mode, T, threads, per_cu, stream);
+        case 4: return launch_epilogue_ch<VPT, 4>(a, mode, T, threads, per_cu, stream);
         default: return hipErrorInvalidValue;  // the pickers choose 2 or 4
     }
 }
@@ -677,80 +667,70 @@ hipError_t launch_epilogue_vpt(const EpilogueArgs& a, EpilogueMode mode, int64_t
 template <int VPT>
 hipError_t launch_qk_vpt(const QkArgs& a, QkMode mode, int64_t T, int threads, hipStream_t stream) {
     switch (mode) {
-        case kQkLocal: return launch_persistent(qk_norm_kernel<VPT, kQkLocal>, a, T, threads, stream);
+        case kQkLocal: return launch_tokens(qk_norm_kernel<VPT, kQkLocal>, a, T, threads, 0, stream);
         case kQkSupplied:
-            return launch_persistent(qk_norm_kernel<VPT, kQkSupplied>, a, T, threads, stream);
+            return launch_tokens(qk_norm_kernel<VPT, kQkSupplied>, a, T, threads, 0, stream);
         case kQkStats:
-            return launch_persistent(qk_norm_kernel<VPT, kQkStats>, a, T, threads, stream);
-        default: return launch_persistent(qk_norm_kernel<VPT, kQkQuant>, a, T, threads, stream);
+            return launch_tokens(qk_norm_kernel<VPT, kQkStats>, a, T, threads, 0, stream);
+        default: return launch_tokens(qk_norm_kernel<VPT, kQkQuant>, a, T, threads, 0, stream);
     }
 }
 
-}  // namespace
-
-namespace {
-
-// Among the allowed (vectors per lane, chunk) pairs: fewest idle lanes first,
-// then the workgroup size nearest 256 threads.
-template <class Allowed>
-LaunchShape pick(int nvec, int ch, Allowed max_threads) {
-    LaunchShape best{0, 0, ch};
-    long best_waste = -1, best_dist = 0;
-    for (int vpt = 1; vpt <= kMaxVpt; ++vpt) {
-        const int limit = max_threads(vpt);
-        if (limit <= 0) continue;
-        const int lanes = (nvec + vpt - 1) / vpt;
-        const int threads = ((lanes + kWave - 1) / kWave) * kWave;
-        if (threads > limit) continue;
-        const long waste = (long)threads * vpt - nvec;
-        const long dist = threads > 256 ? threads - 256 : 256 - threads;
-        if (best_waste < 0 || waste < best_waste || (waste == best_waste && dist < best_dist)) {
-            best = LaunchShape{vpt, threads, ch};
-            best_waste = waste;
-            best_dist = dist;
-        }
-    }
-    return best;
-}
+int round_up_wave(int n) { return (n + kWave - 1) / kWave * kWave; }
 
 }  // namespace
 
 LaunchShape pick_epilogue_shape(int nvec, int P, int64_t T, int cus) {
     if (T <= cus) {
         // Fewer tokens than CUs: each token is one workgroup's whole job, so
-        // spread it over as many lanes as fit (fewest vectors per lane).
+        // spread it over as many lanes as fit (fewest vectors per lane), with
+        // up to four partial buffers' loads in flight at once.
         for (int ch = P <= 2 ? 2 : 4; ch >= 2; ch /= 2) {
             for (int vpt = 1; vpt <= kMaxVpt && vpt * ch <= kMaxLoadsPerLane; ++vpt) {
-                const int threads = ((nvec + vpt - 1) / vpt + kWave - 1) / kWave * kWave;
-                if (threads <= max_threads_for(vpt, ch)) return LaunchShape{vpt, threads, ch};
+                const int threads = round_up_wave((nvec + vpt - 1) / vpt);
+                if (threads <= max_threads_for(vpt, ch)) return LaunchShape{vpt, threads, ch, 0};
             }
         }
-        return LaunchShape{0, 0, 0};
+        return LaunchShape{0, 0, 0, 0};
     }
-    // Measured on MI355X (back-to-back launches, inputs out of cache): the
-    // fastest shapes for the 8192-wide prefill with 8 partials and the
-    // 7168-wide rows with 2 partials.
-    if (nvec == 1024 && P >= 3) return LaunchShape{3, 384, 2};
-    if (nvec == 896 && P <= 2) return LaunchShape{2, 448, 2};
-    // Otherwise: partials two at a time (as fast as four or eight at a time in
-    // those measurements, with fewer registers), fewest idle lanes, then the
-    // workgroup size nearest 256.
-    const LaunchShape s = pick(nvec, 2, [](int vpt) {
-        return vpt * 2 <= kMaxLoadsPerLane ? max_threads_for(vpt, 2) : 0;
-    });
-    return s.vpt > 0 ? s : LaunchShape{0, 0, 0};
+    // Many tokens. Measured on MI355X, inputs out of cache:
+    //  * rows of 32 KB of input per token and more ((P + 1) * H * 2 bytes):
+    //    two resident 384- or 448-thread workgroups per CU looping over tokens
+    //    with next-token prefetch were the fastest for the 8192-wide prefill
+    //    with 8 partials and the 7168-wide rows with 2 partials (inside the
+    //    mixed step of those launches; 256-thread workgroups elsewhere);
+    //  * smaller rows: one token per workgroup of 256 threads (fewer for rows
+    //    of fewer than 256 vectors) ran 1.05x to 1.9x faster than two resident
+    //    workgroups per CU (1024 to 4096 wide, 2 to 8 partials).
+    // Partial buffers are loaded two at a time in both.
+    const int64_t row_in = (int64_t)(P + 1) * nvec * 16;
+    if (row_in >= 32768) {
+        if (nvec == 1024 && P >= 3) return LaunchShape{3, 384, 2, 2};
+        if (nvec == 896) return LaunchShape{2, 448, 2, 2};
+    }
+    const int threads = round_up_wave(nvec < 256 ? nvec : 256);
+    const int vpt = (nvec + threads - 1) / threads;
+    if (vpt > kMaxVpt) return LaunchShape{0, 0, 0, 0};
+    return LaunchShape{vpt, threads, 2, row_in >= 32768 ? 2 : 0};
 }
 
 LaunchShape pick_qk_shape(int nvec, int64_t T, int cus) {
     if (T <= cus) {
         for (int vpt = 1; vpt <= kMaxVpt; ++vpt) {
-            const int threads = ((nvec + vpt - 1) / vpt + kWave - 1) / kWave * kWave;
-            if (threads <= max_threads_for(vpt)) return LaunchShape{vpt, threads, 0};
+            const int threads = round_up_wave((nvec + vpt - 1) / vpt);
+            if (threads <= max_threads_for(vpt)) return LaunchShape{vpt, threads, 0, 0};
         }
-        return LaunchShape{0, 0, 0};
+        return LaunchShape{0, 0, 0, 0};
     }
-    if (nvec == 896) return LaunchShape{4, 256, 0};  // q 6144 + k 1024, measured on MI355X
-    return pick(nvec, 0, [](int vpt) { return max_threads_for(vpt); });
+    // Many tokens: at least two vectors per lane and at most 256 threads.
+    // Measured on MI355X: 128 threads x 2 for 4 KB rows (the MLA rows with FP8
+    // of the q part, the hidden-sharded RMSNorm), 256 x 4 for the 14 KB q | k
+    // rows of the QK norm, each the fastest or within 1% of it.
+    const int half = (nvec + 1) / 2;
+    const int threads = round_up_wave(half < 256 ? half : 256);
+    const int vpt = (nvec + threads - 1) / threads;
+    if (vpt > kMaxVpt) return LaunchShape{0, 0, 0, 0};
+    return LaunchShape{vpt, threads, 0, 0};
 }
 
 hipError_t device_cus(int* cus) {
@@ -763,14 +743,14 @@ hipError_t device_cus(int* cus) {
 hipError_t launch_epilogue(const EpilogueArgs& a, EpilogueMode mode, int64_t T, LaunchShape s,
                            hipStream_t stream) {
     switch (s.vpt) {
-        case 1: return launch_epilogue_vpt<1>(a, mode, T, s.threads, s.ch, stream);
-        case 2: return launch_epilogue_vpt<2>(a, mode, T, s.threads, s.ch, stream);
-        case 3: return launch_epilogue_vpt<3>(a, mode, T, s.threads, s.ch, stream);
-        case 4: return launch_epilogue_vpt<4>(a, mode, T, s.threads, s.ch, stream);
-        case 5: return launch_epilogue_vpt<5>(a, mode, T, s.threads, s.ch, stream);
-        case 6: return launch_epilogue_vpt<6>(a, mode, T, s.threads, s.ch, stream);
-        case 7: return launch_epilogue_vpt<7>(a, mode, T, s.threads, s.ch, stream);
-        case 8: return launch_epilogue_vpt<8>(a, mode, T, s.threads, s.ch, stream);
+        case 1: return launch_epilogue_vpt<1>(a, mode, T, s.threads, s.ch, s.per_cu, stream);
+        case 2: return launch_epilogue_vpt<2>(a, mode, T, s.threads, s.ch, s.per_cu, stream);
+        case 3: return launch_epilogue_vpt<3>(a, mode, T, s.threads, s.ch, s.per_cu, stream);
+        case 4: return launch_epilogue_vpt<4>(a, mode, T, s.threads, s.ch, s.per_cu, stream);
+        case 5: return launch_epilogue_vpt<5>(a, mode, T, s.threads, s.ch, s.per_cu, stream);
+        case 6: return launch_epilogue_vpt<6>(a, mode, T, s.threads, s.ch, s.per_cu, stream);
+        case 7: return launch_epilogue_vpt<7>(a, mode, T, s.threads, s.ch, s.per_cu, stream);
+        case 8: return launch_epilogue_vpt<8>(a, mode, T, s.threads, s.ch, s.per_cu, stream);
         default: return hipErrorInvalidValue;
     }
 }

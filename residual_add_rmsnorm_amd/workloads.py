@@ -15,7 +15,10 @@ QK workloads: qkv = randn(T, row) with its outlier mask; wq = 1 + 0.1 randn(q);
 wk = 1 + 0.1 randn(kv); then tp_world - 1 further shard rows drawn like qkv
 (the other ranks' local rows, used only to form the sum of shard means).
 The MLA all-gather workload draws like a QK workload: the gathered rows
-(q_lora_rank | kv_lora_rank | rope), then the x and y gammas.
+(q_lora_rank | kv_lora_rank | rope), then the x and y gammas. The sharded
+workload: this rank's rows, the weight, then tp_world - 1 further ranks' rows.
+The reduce-scatter workload: P partials of token_num rows, add_in, residual
+and weight (add_in and residual cover the slice only).
 
 The shapes follow the pages' workloads: a 7168-wide decode step, 8192-wide
 prefill with per-token FP8, 7168-wide block-FP8 with 1x128 groups, and the
@@ -36,7 +39,8 @@ import torch
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str                      # "norm", "quant_token", "quant_block", "qk", "mla"
+    kind: str                      # "norm", "quant_token", "quant_block", "quant_static",
+                                   # "rs", "qk", "sharded", "mla"
     T: int
     H: int = 0                     # hidden width (fused epilogue)
     P: int = 0                     # number of partial buffers
@@ -48,6 +52,10 @@ class Workload:
     q_size: int = 0
     kv_size: int = 0
     tp_world: int = 1              # QK mode B: shards folded into the rsqrt
+    token_num: int = 0             # reduce-scatter: tokens in each partial buffer
+    token_offset: int = 0          # reduce-scatter: first token of this GPU's slice
+    pattern: int = 0               # reduce-scatter: fusion pattern code
+    static_scale: float = 0.0      # static FP8: the per-tensor dequantisation scale
     eps: float = 1e-6
     seed: int = 0
     want_norm: bool = True         # FP8 kinds: also write bf16 norm_out (MLA: x_norm_out)
@@ -64,6 +72,11 @@ class Workload:
             write = (self.q_size + self.kv_size) * 2
             var = 8 if self.tp_world > 1 else 0
             return read + write + var
+        if self.kind == "sharded":
+            return self.q_size * 2 + 4 + self.q_size * 2          # row + var_in, out
+        if self.kind == "rs":
+            read = (self.P + 2) * self.H * 2                      # partials, add_in, residual
+            return read + self.H * 2 + self.H + 4 * (self.H // self.group_size)
         if self.kind == "mla":
             read = (self.q_size + self.kv_size) * 2
             write = self.kv_size * 2 + self.q_size + 4 * (self.q_size // self.group_size)
@@ -76,14 +89,16 @@ class Workload:
             write += self.H * 2                              # norm_out
         if self.kind == "quant_token":
             write += self.H + 4
+        elif self.kind == "quant_static":
+            write += self.H
         elif self.kind == "quant_block":
             write += self.H + 4 * (self.H // self.group_size)
         return read + write
 
     def weight_bytes(self) -> int:
-        if self.kind in ("qk", "mla"):
+        if self.kind in ("qk", "mla", "sharded"):
             return (self.q_size + self.kv_size) * 2
-        return self.H * 2
+        return self.H * 2 + (4 if self.kind == "quant_static" else 0)
 
     def algorithmic_bytes(self, T: Optional[int] = None) -> int:
         T = self.T if T is None else T
@@ -113,6 +128,20 @@ WORKLOADS: Dict[str, Workload] = {
         "qk_sharded", "qk", T=4096, row_stride=8192, q_size=6144, kv_size=1024,
         outlier_frac=0.01, outlier_mult=50.0, tp_world=4,
         description="MiniMax QK RMSNorm T=4096, supplied sum of 4 shard means, tp_world=4"),
+    "sharded_post": Workload(
+        "sharded_post", "sharded", T=16384, row_stride=2048, q_size=2048, tp_world=4,
+        outlier_frac=0.01, outlier_mult=50.0,
+        description="sharded-hidden RMSNorm post stage, T=16384 rows of 2048 (8192 over 4 "
+                    "ranks), supplied sum of 4 local means"),
+    "static_fp8": Workload(
+        "static_fp8", "quant_static", T=8192, H=8192, P=8, sigma=0.35, outlier_frac=0.001,
+        outlier_mult=64.0, want_norm=False, static_scale=0.02,
+        description="prefill T=8192 H=8192 P=8 with a static per-tensor e4m3 scale 0.02"),
+    "rs_fp8_block": Workload(
+        "rs_fp8_block", "rs", T=2048, H=7168, P=8, sigma=0.5, token_num=16384,
+        token_offset=6144, pattern=7,
+        description="reduce-scatter epilogue, slice of 2048 of 16384 tokens, H=7168, P=8 "
+                    "peers + add_in, 1x128 e4m3"),
     "mla_ag_fp8": Workload(
         "mla_ag_fp8", "mla", T=8192, row_stride=2112, q_size=1536, kv_size=512,
         outlier_frac=0.001, outlier_mult=64.0, want_norm=False,
@@ -137,6 +166,7 @@ class NormInputs:
     partials: List[torch.Tensor]   # P x bf16 [T, H] (CPU)
     residual: torch.Tensor         # bf16 [T, H]
     weight: torch.Tensor           # bf16 [H]
+    add_in: Optional[torch.Tensor] = None  # reduce-scatter: bf16 [T, H]
 
 
 @dataclass
@@ -155,6 +185,19 @@ def make_inputs(w: Workload, T: Optional[int] = None, seed: Optional[int] = None
         w = w.with_tokens(T)
     gen = torch.Generator(device="cpu")
     gen.manual_seed(w.seed if seed is None else int(seed))
+    if w.kind == "sharded":
+        x = _draw(gen, (w.T, w.row_stride), 1.0, w.outlier_frac, w.outlier_mult)
+        weight = (1.0 + 0.1 * torch.randn(w.q_size, generator=gen)).to(torch.bfloat16)
+        shards = [_draw(gen, (w.T, w.row_stride), 1.0, w.outlier_frac, w.outlier_mult)
+                  for _ in range(w.tp_world - 1)]
+        return QkInputs(w, x, weight, weight[:0], shards)
+    if w.kind == "rs":
+        partials = [_draw(gen, (w.token_num, w.H), w.sigma, w.outlier_frac, w.outlier_mult)
+                    for _ in range(w.P)]
+        add_in = _draw(gen, (w.T, w.H), w.sigma, 0.0, 1.0)
+        residual = _draw(gen, (w.T, w.H), 1.0, 0.0, 1.0)
+        weight = (1.0 + 0.1 * torch.randn(w.H, generator=gen)).to(torch.bfloat16)
+        return NormInputs(w, partials, residual, weight, add_in)
     if w.kind in ("qk", "mla"):
         qkv = _draw(gen, (w.T, w.row_stride), 1.0, w.outlier_frac, w.outlier_mult)
         wq = (1.0 + 0.1 * torch.randn(w.q_size, generator=gen)).to(torch.bfloat16)

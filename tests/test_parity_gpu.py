@@ -359,13 +359,35 @@ def test_qk_empty_and_invalid(fn):
 @pytest.mark.parametrize("H,P", [(8, 1), (1024, 3), (4104, 8), (7168, 2), (8192, 8), (16384, 16),
                                  (1152, 5), (2048, 12)])
 def test_many_tokens_per_workgroup(fn, mode, H, P):
-    """T well above the number of resident workgroups (at most 2 per CU), so each
-    workgroup handles several tokens and prefetches across them."""
+    """T well above the number of CUs. Rows of 32 KB of input per token and more
+    run on two resident workgroups per CU that loop over tokens and prefetch
+    across them (4104 x 8, 7168, 8192, 16384, 2048 x 12); smaller rows run one
+    workgroup per token."""
     if mode == "quant_block" and H % 128:
         pytest.skip("block FP8 needs H % 128 == 0")
     T = 1100 if H <= 8192 else 700
     inp = norm_case(T, H, P, mode, outliers=0.002, seed=H + P)
     check(run_gpu(fn, inp, mode), run_oracle(inp, mode), mode, label=f"{mode} T={T} H={H} P={P}")
+
+
+@pytest.mark.parametrize("mode", ["norm", "quant_token"])
+def test_grid_stride_past_the_grid_limit(fn, mode):
+    """More tokens than the largest grid (2^20 workgroups): the first 37
+    workgroups also take a second token."""
+    T, H, P = (1 << 20) + 37, 8, 1
+    inp = norm_case(T, H, P, mode, seed=5)
+    check(run_gpu(fn, inp, mode), run_oracle(inp, mode), mode, label=f"{mode} T={T} H={H} P={P}")
+
+
+def test_sharded_grid_stride_past_the_grid_limit(fn):
+    T, H = (1 << 20) + 37, 16
+    g = torch.Generator().manual_seed(11)
+    x = torch.randn(T, H, generator=g).to(torch.bfloat16)
+    w = (1 + 0.1 * torch.randn(H, generator=g)).to(torch.bfloat16)
+    out = fn.sharded_rmsnorm(x.to(DEV), w.to(DEV), EPS)
+    torch.cuda.synchronize()
+    ref = oracle.sharded_rmsnorm(wl.bits(x), H, wl.bits(w), EPS)
+    compare_bf16(u16(out), ref["out"], what="sharded out")
 
 
 @pytest.mark.parametrize("q,k,stride,supplied", [(6144, 1024, 8192, False), (6144, 1024, 8192, True),
