@@ -2,9 +2,12 @@
 
 Each case below plants one mistake in a copy of the oracle's C source (a
 dropped term, a wrong index or sign, a transposed operand, a wrong rounding
-rule), builds it on the CPU, and runs the oracle pin tests against that build.
-The pin suite has to fail for every one of them; a mutant that passes means a
-part of the oracle is not pinned.
+rule), builds it on the CPU, and runs the oracle pin tests against that build;
+the Python-level cases plant one mistake in the composition layer
+(oracle/__init__.py: token slicing, operand order, pattern dispatch) and run
+the pins with the mutated module source executed over the real one. The pin
+suite has to fail for every one of them; a mutant that passes means a part of
+the oracle is not pinned.
 """
 import os
 import subprocess
@@ -19,7 +22,8 @@ from oracle import _build
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PIN_FILES = ["tests/test_oracle_codecs.py", "tests/test_oracle_norm.py",
              "tests/test_oracle_quant.py", "tests/test_oracle_qk.py", "tests/test_oracle_sharded.py",
-             "tests/test_oracle_static.py", "tests/test_oracle_ag.py"]
+             "tests/test_oracle_static.py", "tests/test_oracle_ag.py", "tests/test_oracle_rs.py"]
+PY_SRC = os.path.join(ROOT, "oracle", "__init__.py")
 
 # (name, text in the source, replacement)
 MUTANTS = [
@@ -100,6 +104,51 @@ MUTANTS = [
 ]
 
 
+# (name, text in oracle/__init__.py, replacement)
+PY_MUTANTS = [
+    ("RS slice starts one row late",
+     "np.asarray(p)[token_offset:token_offset + T]",
+     "np.asarray(p)[token_offset + 1:token_offset + 1 + T]"),
+    ("RS adds add_in before the partials",
+     "rows.append(_c(add_in, np.uint16))", "rows.insert(0, _c(add_in, np.uint16))"),
+    ("RS adds add_in after the residual",
+     "        rows.append(_c(add_in, np.uint16))\n",
+     "        residual, rows = _c(add_in, np.uint16), rows + [_c(residual, np.uint16)]\n"),
+    ("RS pattern 4 writes no norm",
+     "want_norm=pattern == RS_RESIDUAL_RMSNORM_OUT_FP8", "want_norm=False"),
+    ("RS static patterns ignore the scale",
+     "fused_add_rmsnorm_static(rows, residual, weight, eps, scale_factor,",
+     "fused_add_rmsnorm_static(rows, residual, weight, eps, 1.0,"),
+]
+
+# Runs the pins with a mutated oracle/__init__.py executed over the imported module.
+_PY_DRIVER = """import sys
+import oracle
+exec(compile(open(sys.argv[1]).read(), oracle.__file__, "exec"), oracle.__dict__)
+import pytest
+sys.exit(pytest.main(["-x", "-q", "-p", "no:cacheprovider", *sys.argv[2:]]))
+"""
+
+
+def _run_py_mutant(case, tmp):
+    name, old, new = case
+    with open(PY_SRC) as f:
+        src = f.read()
+    if src.count(old) != 1:
+        return name, "pattern not found exactly once"
+    path = os.path.join(tmp, f"py{abs(hash(name))}.py")
+    with open(path, "w") as f:
+        f.write(src.replace(old, new))
+    env = dict(os.environ, OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-c", _PY_DRIVER, path, *PIN_FILES], cwd=ROOT, env=env,
+                       capture_output=True, text=True, timeout=600)
+    if r.returncode == 0:
+        return name, "SURVIVED: no pin failed"
+    if r.returncode != 1:
+        return name, f"pytest exited {r.returncode}: " + r.stdout[-400:]
+    return name, None
+
+
 def _run_mutant(case, tmp):
     name, old, new = case
     with open(_build.SRC) as f:
@@ -129,6 +178,7 @@ def test_every_planted_mistake_fails_a_pin():
     with tempfile.TemporaryDirectory() as tmp:
         with ThreadPoolExecutor(max_workers=4) as ex:
             results = list(ex.map(lambda c: _run_mutant(c, tmp), MUTANTS))
+            results += list(ex.map(lambda c: _run_py_mutant(c, tmp), PY_MUTANTS))
     bad = [f"{n}: {msg}" for n, msg in results if msg]
     assert not bad, "\n".join(bad)
 
@@ -136,4 +186,10 @@ def test_every_planted_mistake_fails_a_pin():
 @pytest.mark.parametrize("case", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_mutation_pattern_is_present(case):
     with open(_build.SRC) as f:
+        assert f.read().count(case[1]) == 1
+
+
+@pytest.mark.parametrize("case", PY_MUTANTS, ids=[m[0] for m in PY_MUTANTS])
+def test_python_mutation_pattern_is_present(case):
+    with open(PY_SRC) as f:
         assert f.read().count(case[1]) == 1

@@ -7,7 +7,9 @@ Independent facts checked:
   * slice invariance: the epilogue of a token slice equals the whole-batch
     epilogue restricted to those rows;
   * integer inputs give exact sums including add_in;
-  * an all-zero add_in leaves every output of the non-add pattern unchanged.
+  * an all-zero add_in leaves every output of the non-add pattern unchanged;
+  * the static-scale patterns on a row of RMS 1 give hand-known codes for the
+    scale passed in, and pattern 4 also writes the bf16 norm.
 """
 import json
 import os
@@ -90,3 +92,15 @@ def test_static_patterns_and_rejections():
         oracle.rs_epilogue(8, parts, 0, None, res, w, 1e-6)
     with pytest.raises(ValueError):
         oracle.rs_epilogue(3, parts, 0, None, res, w, 1e-6)
+
+
+@pytest.mark.parametrize("pattern", [2, 4])
+def test_static_patterns_hand_row(pattern):
+    # one partial of +-1, zero residual, unit weight, eps 0: y = x, codes = e4m3(x / s)
+    x = np.array([[1, -1, 1, 1, -1, -1, 1, -1]], np.float64)
+    for s_, want in ((0.5, (0x40, 0xC0)), (1.0 / 448.0, (0x7E, 0xFE))):
+        out = oracle.rs_epilogue(pattern, [enc(x)], 0, None, enc(np.zeros_like(x)),
+                                 enc(np.ones(8)), 0.0, scale_factor=s_)
+        assert np.array_equal(out["codes"][0], np.where(x[0] > 0, want[0], want[1]))
+        if pattern == 4:
+            assert np.array_equal(oracle.bf16_decode(out["norm"]), x)
