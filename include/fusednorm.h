@@ -300,6 +300,21 @@ int sharded_rmsnorm_var(const void* x, int64_t T, int64_t row_stride, int64_t H,
  */
 int fusednorm_e4m3_encode(const float* in, void* out, int64_t n, void* stream);
 
+/*
+ * Measurement aids (not part of the method): plain streaming kernels that give
+ * the HBM ceiling next to which the epilogues' bandwidth is reported.
+ *   fusednorm_stream_read  reads `bytes` from src with 16-byte vector loads;
+ *                          sink (4 bytes, device) is written only in a case
+ *                          that no ordinary input reaches
+ *   fusednorm_stream_copy  copies `bytes` from src to dst (no overlap)
+ * bytes must be a positive multiple of 16 KiB; pointers 16-B aligned.
+ * Returns FUSEDNORM_ERR_INVALID_ARGUMENT for NULL pointers or bytes <= 0,
+ * FUSEDNORM_ERR_UNSUPPORTED for other unsupported sizes, alignment or overlap,
+ * FUSEDNORM_ERR_HIP for a launch error. They do not set fusednorm_last_error.
+ */
+int fusednorm_stream_read(const void* src, int64_t bytes, void* sink, void* stream);
+int fusednorm_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
 /* Static description of a status code. Never NULL. */
 const char* fusednorm_status_string(int status);
 

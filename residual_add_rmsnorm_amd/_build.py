@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfusednorm.so")
-SOURCES = [os.path.join(CSRC, "fusednorm_kernels.hip"), os.path.join(CSRC, "fusednorm_api.cpp")]
+SOURCES = [os.path.join(CSRC, "fusednorm_kernels.hip"), os.path.join(CSRC, "fusednorm_api.cpp"),
+           os.path.join(CSRC, "fusednorm_stream.hip")]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

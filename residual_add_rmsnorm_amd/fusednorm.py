@@ -65,6 +65,8 @@ def _load() -> ctypes.CDLL:
         "sharded_rmsnorm": [vp, i64, i64, i64, vp, f32, i32, vp, vp, vp],
         "sharded_rmsnorm_var": [vp, i64, i64, i64, vp, vp],
         "fusednorm_e4m3_encode": [vp, vp, i64, vp],
+        "fusednorm_stream_read": [vp, i64, vp, vp],
+        "fusednorm_stream_copy": [vp, vp, i64, vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -517,10 +519,34 @@ def e4m3_encode(x: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None
     return out
 
 
+def stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Measurement aid: reads all of ``src`` (nbytes a multiple of 16 KiB) with
+    plain 16-byte vector loads; ``sink`` is a 4-byte device buffer."""
+    _need(src, "src", dtype=None)
+    _need(sink, "sink", dtype=None)
+    if sink.nbytes < 4:
+        raise ValueError("sink must hold 4 bytes")
+    rc = _lib.fusednorm_stream_read(_ptr(src), src.nbytes, _ptr(sink), _stream(src.device, stream))
+    if rc != FUSEDNORM_OK:
+        raise FusedNormError("fusednorm_stream_read", rc, "")
+
+
+def stream_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    """Measurement aid: copies ``src`` to ``dst`` (same size, a multiple of
+    16 KiB) with plain 16-byte vector loads and stores."""
+    _need(src, "src", dtype=None)
+    _need(dst, "dst", dtype=None)
+    if dst.nbytes != src.nbytes:
+        raise ValueError("src and dst must have the same size")
+    rc = _lib.fusednorm_stream_copy(_ptr(src), _ptr(dst), src.nbytes, _stream(src.device, stream))
+    if rc != FUSEDNORM_OK:
+        raise FusedNormError("fusednorm_stream_copy", rc, "")
+
+
 __all__ = [
     "fused_add_rmsnorm", "fused_add_rmsnorm_quant_fp8", "fused_add_rmsnorm_quant_fp8_block",
     "fused_add_rmsnorm_quant_fp8_static", "fused_rs_epilogue", "ag_dual_rmsnorm",
     "qk_rmsnorm", "qk_rmsnorm_var", "sharded_rmsnorm", "sharded_rmsnorm_var", "e4m3_encode",
-    "version", "library_path",
+    "stream_read", "stream_copy", "version", "library_path",
     "FusedNormError", "FusedNormUnsupported", "FusedNormLibraryMissing",
 ]

@@ -312,3 +312,15 @@ def test_ag_dual_validation(lib):
     assert call(2, x=None, codes=addr(5, 4), scale=sc) == 2
     assert call(y=addr(1, 64)) == 2 and "overlaps" in last(lib)
     assert call(2, x=None, codes=addr(4, 64), scale=sc) == 2 and "overlaps" in last(lib)
+
+
+def test_stream_aid_validation(lib):
+    rd, cp = lib.fusednorm_stream_read, lib.fusednorm_stream_copy
+    K16 = 16 * 1024
+    assert rd(None, K16, addr(2), None) == 1
+    assert rd(addr(1), 0, addr(2), None) == 1
+    assert rd(addr(1), K16 + 16, addr(2), None) == 2
+    assert rd(addr(1, 8), K16, addr(2), None) == 2
+    assert cp(addr(1), None, K16, None) == 1
+    assert cp(addr(1), addr(1, K16 // 2), K16, None) == 2      # overlapping
+    assert cp(addr(1), addr(2, 4), K16, None) == 2

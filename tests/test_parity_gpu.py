@@ -611,3 +611,14 @@ def test_ag_dual_rmsnorm(fn, T, q, kv, stride, quant):
         say(f"ag q={q} kv={kv} stride={stride} T={T}:",
             compare_e4m3(u8(out["codes"]), ref["codes"], ref["near_tie"]))
 
+
+
+def test_stream_aids(fn):
+    # the measurement aids: the copy reproduces its input, the read runs cleanly
+    src = torch.arange(3 * 8192, dtype=torch.int32, device=DEV)       # 96 KiB
+    dst = torch.empty_like(src)
+    fn.stream_copy(src, dst)
+    sink = torch.zeros(1, dtype=torch.int32, device=DEV)
+    fn.stream_read(src, sink)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
