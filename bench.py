@@ -190,10 +190,16 @@ def cpu_baseline(parts, min_seconds=10.0, max_reps=8):
             if reps == 0:
                 log(f"[bench] cpu oracle {p.name}: {dt:.2f} s")
         reps += 1
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next(ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     return {"value": round(reps * step_bytes / total_s / 1e9, 3), "unit": "GB/s",
             "cores": oracle.max_threads(), "kind": "oracle",
             "sample": f"{reps} full steps (all four launches, every token) on the host, "
-                      f"{total_s:.1f} s in all"}
+                      f"{total_s:.1f} s in all; {model}, {os.cpu_count()} logical CPUs visible"}
 
 
 def ceilings(fn, torch, dev, reps=10):
