@@ -622,3 +622,79 @@ def test_stream_aids(fn):
     fn.stream_read(src, sink)
     torch.cuda.synchronize()
     assert torch.equal(src, dst)
+
+
+# ----------------------------------------------------------------------------- further entry points, full size
+
+def _sample_rows(T, n=256, seed=6):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, T - 1], rng.choice(T, min(n, T), replace=False)]))
+
+
+def test_next_sharded_post_full_size(fn):
+    """The sharded post stage as the benchmark launches it (16384 rows of 2048,
+    supplied sum of 4 ranks' local means); every row against the oracle."""
+    w = wl.WORKLOADS["sharded_post"]
+    inp = wl.make_inputs(w)
+    H = w.q_size
+    bits = [wl.bits(inp.qkv)] + [wl.bits(s) for s in inp.shards]
+    var_in = sum(oracle.sharded_means(b, H) for b in bits).astype(np.float32)
+    out = fn.sharded_rmsnorm(inp.qkv.to(DEV), inp.q_weight.to(DEV), w.eps, w.tp_world,
+                             torch.from_numpy(var_in).to(DEV), H=H)
+    torch.cuda.synchronize()
+    ref = oracle.sharded_rmsnorm(bits[0], H, wl.bits(inp.q_weight), w.eps, w.tp_world, var_in)
+    say("sharded_post full size:", compare_bf16(u16(out), ref["out"], what="out"))
+
+
+def test_next_static_fp8_full_size_sampled(fn):
+    w = wl.WORKLOADS["static_fp8"]
+    say(f"[static_fp8] drawing T={w.T} H={w.H} P={w.P}")
+    inp = wl.make_inputs(w)
+    q, rout, _ = fn.fused_add_rmsnorm_quant_fp8_static(
+        [p.to(DEV) for p in inp.partials], inp.residual.to(DEV), inp.weight.to(DEV),
+        torch.tensor([w.static_scale], dtype=torch.float32, device=DEV), w.eps)
+    torch.cuda.synchronize()
+    rows = _sample_rows(w.T)
+    ref = oracle.fused_add_rmsnorm_static([wl.bits(p)[rows] for p in inp.partials],
+                                          wl.bits(inp.residual)[rows], wl.bits(inp.weight), w.eps,
+                                          w.static_scale)
+    compare_bf16(u16(rout)[rows], ref["residual"], max_ulp=0, what="residual_out")
+    say(f"static_fp8 full size, {len(rows)} rows:",
+        compare_e4m3(u8(q)[rows], ref["codes"], ref["near_tie"]))
+
+
+def test_next_rs_fp8_block_full_size(fn):
+    """Pattern 7 on the benchmark's slice (2048 of 16384 tokens, 8 partials +
+    add_in); every row of the slice against the oracle."""
+    w = wl.WORKLOADS["rs_fp8_block"]
+    inp = wl.make_inputs(w)
+    out = fn.fused_rs_epilogue(w.pattern, [p.to(DEV) for p in inp.partials], w.token_offset,
+                               inp.residual.to(DEV), inp.weight.to(DEV), w.eps,
+                               add_in=inp.add_in.to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.rs_epilogue(w.pattern, [wl.bits(p) for p in inp.partials], w.token_offset,
+                             wl.bits(inp.add_in), wl.bits(inp.residual), wl.bits(inp.weight), w.eps)
+    compare_bf16(u16(out["residual"]), ref["residual"], max_ulp=0, what="residual_out")
+    compare_scales(out["scales"].cpu().numpy(), ref["scales"])
+    say("rs_fp8_block full size:", compare_e4m3(u8(out["codes"]), ref["codes"], ref["near_tie"]))
+
+
+def test_next_mla_full_size(fn):
+    """The MLA epilogue as the benchmark launches it (8192 rows, pattern 2,
+    no x_norm_out), then pattern 1; every row against the oracle."""
+    w = wl.WORKLOADS["mla_ag_fp8"]
+    inp = wl.make_inputs(w)
+    rows = inp.qkv.to(DEV)
+    gx, gy = inp.q_weight.to(DEV), inp.k_weight.to(DEV)
+    two = fn.ag_dual_rmsnorm(rows, w.q_size, w.kv_size, gx, gy, w.eps, w.eps, quant=True,
+                             want_x=False)
+    one = fn.ag_dual_rmsnorm(rows, w.q_size, w.kv_size, gx, gy, w.eps, w.eps)
+    torch.cuda.synchronize()
+    b = wl.bits(inp.qkv)
+    ref = oracle.ag_dual_rmsnorm(b, w.q_size, w.kv_size, wl.bits(inp.q_weight),
+                                 wl.bits(inp.k_weight), w.eps, w.eps, quant=True)
+    compare_bf16(u16(two["y"]), ref["y"], what="y_norm_out")
+    compare_bf16(u16(one["y"]), ref["y"], what="y_norm_out (pattern 1)")
+    compare_bf16(u16(one["x"]), ref["x"], what="x_norm_out (pattern 1)")
+    compare_scales(two["scales"].cpu().numpy(), ref["scales"])
+    say("mla full size:", compare_e4m3(u8(two["codes"]), ref["codes"], ref["near_tie"]))
