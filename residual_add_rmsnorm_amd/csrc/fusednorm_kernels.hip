@@ -8,11 +8,10 @@
 // and the vLLM minimax_rms_norm/rms_norm_tp page (_minimax_qk_var_kernel,
 // _minimax_rms_apply_kernel). How it is computed is designed for CDNA4:
 //
-//   * the grid: for rows of 32 KB of input and more per token, two resident
-//     workgroups per CU, each looping over tokens and issuing the next
-//     token's loads as soon as the current token's sum is formed; for smaller
-//     rows (and the QK family), one workgroup per token, the hardware
-//     dispatcher keeping every CU filled as workgroups finish;
+//   * the grid: one workgroup per token, the hardware dispatcher keeping every
+//     CU filled as workgroups finish; for the 7168-wide rows, two resident
+//     workgroups per CU, each looping over tokens and issuing the next token's
+//     loads as soon as the current token's sum is formed;
 //   * a token's row is cut into 16-byte vectors (8 bf16); vector i belongs to
 //     lane i mod blockDim, slot i / blockDim, so every wave-wide access covers
 //     1 KiB of consecutive bytes, read and written through per-row buffer
@@ -693,25 +692,19 @@ LaunchShape pick_epilogue_shape(int nvec, int P, int64_t T, int cus) {
         }
         return LaunchShape{0, 0, 0, 0};
     }
-    // Many tokens. Measured on MI355X, inputs out of cache:
-    //  * rows of 32 KB of input per token and more ((P + 1) * H * 2 bytes):
-    //    two resident 384- or 448-thread workgroups per CU looping over tokens
-    //    with next-token prefetch were the fastest for the 8192-wide prefill
-    //    with 8 partials and the 7168-wide rows with 2 partials (inside the
-    //    mixed step of those launches; 256-thread workgroups elsewhere);
-    //  * smaller rows: one token per workgroup of 256 threads (fewer for rows
-    //    of fewer than 256 vectors) ran 1.05x to 1.9x faster than two resident
-    //    workgroups per CU (1024 to 4096 wide, 2 to 8 partials).
-    // Partial buffers are loaded two at a time in both.
-    const int64_t row_in = (int64_t)(P + 1) * nvec * 16;
-    if (row_in >= 32768) {
-        if (nvec == 1024 && P >= 3) return LaunchShape{3, 384, 2, 2};
-        if (nvec == 896) return LaunchShape{2, 448, 2, 2};
-    }
+    // Many tokens. Measured on MI355X, inputs out of cache: one workgroup per
+    // token, 256 threads (fewer for rows of fewer than 256 vectors), partials
+    // two buffers at a time, was the fastest shape or within 1% of it for rows
+    // of 1024 to 16384 elements with 2 to 16 partials, 1.05x to 1.9x faster
+    // than two resident workgroups per CU looping over tokens. The exception is
+    // the 7168-wide rows: there two resident 448-thread workgroups per CU with
+    // next-token prefetch ran 6% faster inside the benchmark step (block FP8,
+    // 2 partials), as fast for 4 and 9 partials.
+    if (nvec == 896) return LaunchShape{2, 448, 2, 2};
     const int threads = round_up_wave(nvec < 256 ? nvec : 256);
     const int vpt = (nvec + threads - 1) / threads;
     if (vpt > kMaxVpt) return LaunchShape{0, 0, 0, 0};
-    return LaunchShape{vpt, threads, 2, row_in >= 32768 ? 2 : 0};
+    return LaunchShape{vpt, threads, 2, 0};
 }
 
 LaunchShape pick_qk_shape(int nvec, int64_t T, int cus) {

@@ -359,10 +359,9 @@ def test_qk_empty_and_invalid(fn):
 @pytest.mark.parametrize("H,P", [(8, 1), (1024, 3), (4104, 8), (7168, 2), (8192, 8), (16384, 16),
                                  (1152, 5), (2048, 12)])
 def test_many_tokens_per_workgroup(fn, mode, H, P):
-    """T well above the number of CUs. Rows of 32 KB of input per token and more
-    run on two resident workgroups per CU that loop over tokens and prefetch
-    across them (4104 x 8, 7168, 8192, 16384, 2048 x 12); smaller rows run one
-    workgroup per token."""
+    """T well above the number of CUs. The 7168-wide rows run on two resident
+    workgroups per CU that loop over tokens and prefetch across them; the
+    others run one workgroup per token."""
     if mode == "quant_block" and H % 128:
         pytest.skip("block FP8 needs H % 128 == 0")
     T = 1100 if H <= 8192 else 700
