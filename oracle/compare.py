@@ -35,6 +35,8 @@ class Bf16Report:
     max_rel: float
 
     def __str__(self):
+        if self.n_diff == 0:
+            return f"bf16: {self.n} values, all bit-identical"
         return (f"bf16: {self.n} values, {self.n_diff} differ by <= {self.max_ulp} ulp, "
                 f"max rel {self.max_rel:.3g}")
 
