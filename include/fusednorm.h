@@ -9,10 +9,13 @@
  *                (amd_allreduce_residual_rmsnorm_kernel and its dispatcher
  *                allreduce_residual_rmsnorm / allreduce_residual_rmsnorm_can_run).
  *   [TS-TRTLLM]  lightseekorg--tokenspeed, tokenspeed_kernel/thirdparty/cuda/
- *                trtllm.py, sections "Pattern enums" (AllReduceFusionPattern),
- *                "AllReduce fusion" (trtllm_allreduce_fusion), "AllGather
- *                fusion" (the 128-wide FP8 block) and "MiniMax QK fused AR +
- *                RMSNorm" (minimax_allreduce_rms_qk).
+ *                trtllm.py, sections "Pattern enums" (AllReduceFusionPattern,
+ *                AllGatherFusionPattern, ReduceScatterFusionPattern),
+ *                "AllReduce fusion" (trtllm_allreduce_fusion and its static
+ *                scale_factor), "AllGather fusion" (trtllm_allgather_fusion, the
+ *                128-wide FP8 block), "ReduceScatter fusion"
+ *                (trtllm_reducescatter_fusion) and "MiniMax QK fused AR +
+ *                RMSNorm" (minimax_allreduce_rms_qk, minimax_allreduce_rms).
  *   [VLLM-QK]    vLLM API docs, vllm.model_executor.layers.minimax_rms_norm.
  *                rms_norm_tp (_minimax_qk_norm_tp_eager, _minimax_qk_var_kernel,
  *                _minimax_rms_apply_kernel).
@@ -22,10 +25,12 @@
  *     16-bit storage, FP8 as one byte per value in OCP E4M3 ("e4m3fn": bias 7,
  *     largest finite 448, no infinities, S.1111.111 = NaN).
  *   - The caller owns and allocates every buffer; the library allocates no
- *     device or host memory, keeps no state between calls and never
- *     synchronises. Work is enqueued on `stream` (a hipStream_t; NULL = the
- *     default stream) on the current device; results are ready when that stream
- *     reaches the work. Calls are thread-safe and reentrant.
+ *     device memory and never synchronises. Its only state is a small host-side
+ *     cache, per device, of the CU count and the kernels' occupancy (filled on
+ *     first use, guarded by a mutex) and the calling thread's last error text.
+ *     Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) on
+ *     the current device; results are ready when that stream reaches the work.
+ *     Calls are thread-safe and reentrant.
  *   - Every argument is validated before anything is launched; on any error
  *     nothing is launched and nothing is written. T == 0 (n == 0) is valid:
  *     once the scalar arguments are checked the call returns FUSEDNORM_OK

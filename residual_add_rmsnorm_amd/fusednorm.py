@@ -265,8 +265,10 @@ def fused_add_rmsnorm_quant_fp8_static(partials, residual: torch.Tensor, weight:
                                        residual_out: Optional[torch.Tensor] = None,
                                        quant_out: Optional[torch.Tensor] = None, stream=None):
     """Fused epilogue + OCP e4m3 with one static dequantisation scale for the
-    tensor (a float or a one-element fp32 GPU tensor, as the pages accept).
-    Returns (quant_out e4m3 [T,H], residual_out, norm_out or None)."""
+    tensor (a float or a one-element fp32 GPU tensor, as the pages accept; a
+    float is copied to the device on every call, so pass a tensor in loops and
+    under graph capture). Returns (quant_out e4m3 [T,H], residual_out, norm_out
+    or None)."""
     parts, arr = _partials(partials)
     _need(residual, "residual")
     _need(weight, "weight")
@@ -302,8 +304,9 @@ def fused_rs_epilogue(pattern: int, partials, token_offset: int, residual: torch
                       quant_out: Optional[torch.Tensor] = None,
                       scale_out: Optional[torch.Tensor] = None, stream=None) -> dict:
     """Reduce-scatter epilogue on rows [token_offset, token_offset + T) of the
-    partial buffers (each [token_num, H]); T = residual.shape[0]. Returns a dict
-    with the outputs the pattern writes."""
+    partial buffers (each [token_num, H]); T = residual.shape[0]. Patterns 2
+    and 4 take scale_factor as fused_add_rmsnorm_quant_fp8_static does. Returns
+    a dict with the outputs the pattern writes."""
     if pattern not in RS_PATTERNS:
         raise FusedNormUnsupported("fused_rs_epilogue", FUSEDNORM_ERR_UNSUPPORTED,
                                    f"pattern {pattern} is not implemented")
