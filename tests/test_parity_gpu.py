@@ -493,6 +493,69 @@ def test_graph_capture_replays_match_eager(fn):
 
 
 
+
+def test_graph_capture_further_entry_points(fn):
+    """The sharded stages, static-scale FP8, the reduce-scatter epilogue (on
+    the persistent 7168-wide grid) and the MLA epilogue captured in one HIP
+    graph: every replay, between eager runs, equals the eager result."""
+    g_ = torch.Generator().manual_seed(21)
+    x = torch.randn(700, 2048, generator=g_).to(torch.bfloat16).to(DEV)
+    wx = torch.ones(2048, dtype=torch.bfloat16, device=DEV)
+    st = norm_case(600, 8192, 4, "quant_token", seed=22)
+    st_dev = ([p.to(DEV) for p in st.partials], st.residual.to(DEV), st.weight.to(DEV))
+    scale = torch.tensor([0.02], dtype=torch.float32, device=DEV)
+    rs_parts = [(torch.randn(1500, 7168, generator=g_) * 0.5).to(torch.bfloat16).to(DEV)
+                for _ in range(3)]
+    rs_add = torch.randn(900, 7168, generator=g_).to(torch.bfloat16).to(DEV)
+    rs_res = torch.randn(900, 7168, generator=g_).to(torch.bfloat16).to(DEV)
+    rs_w = torch.ones(7168, dtype=torch.bfloat16, device=DEV)
+    mla_rows = torch.randn(800, 2112, generator=g_).to(torch.bfloat16).to(DEV)
+    gx = torch.ones(1536, dtype=torch.bfloat16, device=DEV)
+    gy = torch.ones(512, dtype=torch.bfloat16, device=DEV)
+    outs = dict(
+        var=torch.empty(700, device=DEV), sh=torch.empty(700, 2048, dtype=torch.bfloat16, device=DEV),
+        st_q=torch.empty(600, 8192, dtype=torch.uint8, device=DEV), st_r=torch.empty_like(st_dev[1]),
+        rs_r=torch.empty_like(rs_res), rs_q=torch.empty(900, 7168, dtype=torch.uint8, device=DEV),
+        rs_s=torch.empty(900, 56, device=DEV),
+        y=torch.empty(800, 512, dtype=torch.bfloat16, device=DEV),
+        c=torch.empty(800, 1536, dtype=torch.uint8, device=DEV), cs=torch.empty(800, 12, device=DEV))
+
+    def step():
+        fn.sharded_rmsnorm_var(x, var_out=outs["var"])
+        fn.sharded_rmsnorm(x, wx, EPS, 1, outs["var"], out=outs["sh"])
+        fn.fused_add_rmsnorm_quant_fp8_static(*st_dev, scale, EPS, residual_out=outs["st_r"],
+                                              quant_out=outs["st_q"])
+        fn.fused_rs_epilogue(7, rs_parts, 550, rs_res, rs_w, EPS, add_in=rs_add,
+                             residual_out=outs["rs_r"], quant_out=outs["rs_q"],
+                             scale_out=outs["rs_s"])
+        fn.ag_dual_rmsnorm(mla_rows, 1536, 512, gx, gy, EPS, EPS, quant=True, want_x=False,
+                           y_norm_out=outs["y"], quant_out=outs["c"], scale_out=outs["cs"])
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return [t.clone() for t in outs.values()]
+
+    step()
+    eager = snapshot()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for k in range(4):
+        for t in outs.values():
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        for name, a, e in zip(outs, snapshot(), eager):
+            assert torch.equal(a, e), f"replay {k}: {name} differs from the eager result"
+        step()
+        torch.cuda.synchronize()
+
 # ----------------------------------------------------------------------------- sharded-hidden RMSNorm
 
 @pytest.mark.parametrize("T", [1, 37, 1500])
