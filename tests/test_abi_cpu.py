@@ -324,3 +324,18 @@ def test_stream_aid_validation(lib):
     assert cp(addr(1), None, K16, None) == 1
     assert cp(addr(1), addr(1, K16 // 2), K16, None) == 2      # overlapping
     assert cp(addr(1), addr(2, 4), K16, None) == 2
+
+
+def test_c_client_compiles_as_c_and_runs(lib, tmp_path):
+    """The header is plain C and the library links from C; the client makes only
+    calls that return before any HIP work."""
+    from residual_add_rmsnorm_amd import _build
+    exe = tmp_path / "abi_check"
+    src = os.path.join(ROOT, "residual_add_rmsnorm_amd", "examples", "abi_check.c")
+    libdir = os.path.dirname(_build.LIB)
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Wextra", "-Werror", "-I",
+                    os.path.join(ROOT, "include"), src, "-L", libdir, "-lfusednorm",
+                    f"-Wl,-rpath,{libdir}", "-o", str(exe)], check=True, capture_output=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert r.stdout.strip().endswith("ok")
