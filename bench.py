@@ -307,9 +307,9 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
-              f"WORLD_SIZE={world}); the multi-GPU exchange is not built, so there is no "
-              "figure at more than one GPU.", file=sys.stderr)
+        print(f"bench.py: libfusednorm runs on one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE={world}); the multi-GPU exchange is not implemented, so there is "
+              "no figure at more than one GPU.", file=sys.stderr)
         sys.exit(2)
 
     import torch

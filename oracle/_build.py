@@ -1,7 +1,7 @@
 """Builds the CPU oracle (plain C, gcc, OpenMP) into oracle/liboracle.so.
 
-Test infrastructure: the oracle is built here so that the checker exists; the
-product library never links or loads it.
+Test infrastructure: the oracle is built here for the tests, the smoke check and
+the benchmark's CPU baseline; the product library never links or loads it.
 """
 import os
 import subprocess
