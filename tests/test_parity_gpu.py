@@ -760,3 +760,39 @@ def test_next_mla_full_size(fn):
     compare_bf16(u16(one["x"]), ref["x"], what="x_norm_out (pattern 1)")
     compare_scales(two["scales"].cpu().numpy(), ref["scales"])
     say("mla full size:", compare_e4m3(u8(two["codes"]), ref["codes"], ref["near_tie"]))
+
+
+_FIRST_CALL_UNDER_CAPTURE = r"""
+import sys, torch
+sys.path.insert(0, sys.argv[1])
+from residual_add_rmsnorm_amd import fusednorm as fn
+dev = "cuda:0"
+g = torch.Generator().manual_seed(3)
+parts = [torch.randn(600, 7168, generator=g).to(torch.bfloat16).to(dev) for _ in range(2)]
+res = torch.randn(600, 7168, generator=g).to(torch.bfloat16).to(dev)
+w = torch.ones(7168, dtype=torch.bfloat16, device=dev)
+q = torch.empty(600, 7168, dtype=torch.uint8, device=dev)
+s = torch.empty(600, 56, device=dev)
+r = torch.empty_like(res)
+graph = torch.cuda.CUDAGraph()
+with torch.cuda.graph(graph):   # the library's first call in this process
+    fn.fused_add_rmsnorm_quant_fp8_block(parts, res, w, 1e-6, residual_out=r, quant_out=q, scale_out=s)
+graph.replay()
+torch.cuda.synchronize()
+got = (r.clone(), q.clone(), s.clone())
+fn.fused_add_rmsnorm_quant_fp8_block(parts, res, w, 1e-6, residual_out=r, quant_out=q, scale_out=s)
+torch.cuda.synchronize()
+assert all(torch.equal(a, b) for a, b in zip(got, (r, q, s))), "graph replay differs from eager"
+print("ok", flush=True)
+"""
+
+
+def test_first_call_inside_a_graph_capture():
+    """A process whose first library call is captured (the persistent 7168-wide
+    grid queries the kernel's occupancy on first use) replays correctly."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", _FIRST_CALL_UNDER_CAPTURE, root], capture_output=True,
+                       text=True, timeout=240)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout[-2000:] + r.stderr[-2000:]
