@@ -796,3 +796,76 @@ def test_first_call_inside_a_graph_capture():
     r = subprocess.run([sys.executable, "-c", _FIRST_CALL_UNDER_CAPTURE, root], capture_output=True,
                        text=True, timeout=240)
     assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout[-2000:] + r.stderr[-2000:]
+
+
+# ----------------------------------------------------------------------------- seeded random shapes
+
+def _random_epilogue_case(seed):
+    """Seeded random valid shape: mode, H (a multiple of 8, of 128 for block
+    FP8), P in 1..16, T up to 3000, optional norm_out; at most ~2^25 elements
+    over all buffers so the oracle stays quick."""
+    rng = np.random.default_rng(1000 + seed)
+    mode = ["norm", "quant_token", "quant_block"][seed % 3]
+    P = int(rng.integers(1, 17))
+    H = int(rng.integers(1, 129)) * 128 if mode == "quant_block" else int(rng.integers(1, 2049)) * 8
+    tmax = max(1, min(3000, (1 << 25) // (H * (P + 3))))
+    T = int(rng.integers(1, tmax + 1))
+    return mode, T, H, P, bool(rng.integers(0, 2))
+
+
+@pytest.mark.parametrize("seed", range(18))
+def test_random_shapes_epilogue(fn, seed):
+    mode, T, H, P, want_norm = _random_epilogue_case(seed)
+    inp = norm_case(T, H, P, mode, sigma=0.5, outliers=0.001, seed=seed)
+    want_norm = want_norm or mode == "norm"
+    check(run_gpu(fn, inp, mode, want_norm), run_oracle(inp, mode, want_norm), mode, want_norm,
+          label=f"seed {seed}: {mode} T={T} H={H} P={P} norm_out={want_norm}")
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shapes_qk_family(fn, seed):
+    """Seeded random QK, sharded and MLA shapes, strides and token counts."""
+    rng = np.random.default_rng(2000 + seed)
+    kind = ["qk", "sharded", "mla"][seed % 3]
+    q = int(rng.integers(1, 97)) * 128 if kind == "mla" else int(rng.integers(1, 1025)) * 8
+    k = 0 if kind == "sharded" else int(rng.integers(1, 257)) * 8
+    if q + k > 16384:
+        q = 16384 - k - (16384 - k) % (128 if kind == "mla" else 8)
+    stride = q + k + int(rng.integers(0, 33)) * 8
+    T = int(rng.integers(1, max(2, min(3000, (1 << 24) // stride)) + 1))
+    g = torch.Generator().manual_seed(3000 + seed)
+    rows = torch.randn(T, stride, generator=g).to(torch.bfloat16)
+    rows[:, q + k:] = float("nan")                       # past the segments: never read
+    wq = (1 + 0.1 * torch.randn(q, generator=g)).to(torch.bfloat16)
+    wk = (1 + 0.1 * torch.randn(max(k, 1), generator=g)).to(torch.bfloat16)[:k]
+    b = wl.bits(rows)
+    label = f"seed {seed}: {kind} T={T} q={q} k={k} stride={stride}"
+    if kind == "qk":
+        tp = int(rng.integers(1, 5))
+        var = None if tp == 1 else (oracle.qk_means(b, q, k) * tp).astype(np.float32)
+        qo, ko = fn.qk_rmsnorm(rows.to(DEV), q, k, wq.to(DEV), wk.to(DEV), EPS, tp,
+                               None if var is None else torch.from_numpy(var).to(DEV))
+        torch.cuda.synchronize()
+        ref = oracle.qk_rmsnorm(b, q, k, wl.bits(wq), wl.bits(wk), EPS, tp, var)
+        compare_bf16(u16(qo), ref["q"], what="q_out")
+        say(label, compare_bf16(u16(ko), ref["k"], what="k_out"))
+    elif kind == "sharded":
+        tp = int(rng.integers(1, 9))
+        var = None if tp == 1 else (oracle.sharded_means(b, q) * tp).astype(np.float32)
+        out = fn.sharded_rmsnorm(rows.to(DEV), wq.to(DEV), EPS, tp,
+                                 None if var is None else torch.from_numpy(var).to(DEV), H=q)
+        torch.cuda.synchronize()
+        ref = oracle.sharded_rmsnorm(b, q, wl.bits(wq), EPS, tp, var)
+        say(label, compare_bf16(u16(out), ref["out"], what="out"))
+    else:
+        quant = bool(rng.integers(0, 2))
+        out = fn.ag_dual_rmsnorm(rows.to(DEV), q, k, wq.to(DEV), wk.to(DEV), 1e-6, 0.01,
+                                 quant=quant)
+        torch.cuda.synchronize()
+        ref = oracle.ag_dual_rmsnorm(b, q, k, wl.bits(wq), wl.bits(wk), 1e-6, 0.01, quant=quant)
+        compare_bf16(u16(out["x"]), ref["x"], what="x_norm_out")
+        rep = compare_bf16(u16(out["y"]), ref["y"], what="y_norm_out")
+        if quant:
+            compare_scales(out["scales"].cpu().numpy(), ref["scales"])
+            rep = compare_e4m3(u8(out["codes"]), ref["codes"], ref["near_tie"])
+        say(label, rep)
