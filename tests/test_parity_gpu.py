@@ -869,3 +869,77 @@ def test_random_shapes_qk_family(fn, seed):
             compare_scales(out["scales"].cpu().numpy(), ref["scales"])
             rep = compare_e4m3(u8(out["codes"]), ref["codes"], ref["near_tie"])
         say(label, rep)
+
+
+# ----------------------------------------------------------------------------- nothing written past the outputs
+
+GUARD = 4096   # elements of sentinel after each output
+
+
+def _guarded(shape, dtype, fill):
+    n = int(np.prod(shape))
+    buf = torch.full((n + GUARD,), fill, dtype=dtype, device=DEV)
+    return buf, buf[:n].view(*shape)
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+@pytest.mark.parametrize("T,H,P", [(37, 7168, 3), (300, 7168, 2), (300, 1000, 5), (37, 4104, 8),
+                                   (600, 16384, 2)])
+def test_no_write_past_the_outputs(fn, mode, T, H, P):
+    """Lanes past a row's end (e.g. 7168-wide rows on 256-thread workgroups) and
+    the last token write nothing beyond the outputs: guard bands keep their
+    sentinels."""
+    if mode == "quant_block" and H % 128:
+        pytest.skip("block FP8 needs H % 128 == 0")
+    inp = norm_case(T, H, P, mode, seed=T + H)
+    parts = [p.to(DEV) for p in inp.partials]
+    res, w = inp.residual.to(DEV), inp.weight.to(DEV)
+    rb, rout = _guarded((T, H), torch.bfloat16, 3.0)
+    nb, norm = _guarded((T, H), torch.bfloat16, 3.0)
+    if mode == "norm":
+        fn.fused_add_rmsnorm(parts, res, w, EPS, norm_out=norm, residual_out=rout)
+        guards = [rb, nb]
+    else:
+        qb, q = _guarded((T, H), torch.uint8, 0x5A)
+        groups = H // 128 if mode == "quant_block" else 0
+        sb, sc = _guarded((T, groups) if groups else (T,), torch.float32, -7.0)
+        f = fn.fused_add_rmsnorm_quant_fp8 if mode == "quant_token" else \
+            fn.fused_add_rmsnorm_quant_fp8_block
+        f(parts, res, w, EPS, norm_out=norm, residual_out=rout, quant_out=q, scale_out=sc)
+        guards = [rb, nb, qb, sb]
+    torch.cuda.synchronize()
+    for g in guards:
+        tail = g[-GUARD:]
+        assert torch.all(tail == tail[0]) and float(tail[0]) in (3.0, 0x5A, -7.0), \
+            "an output's guard band was written"
+    check(dict(residual=rout, norm=norm, **({} if mode == "norm" else dict(codes=q, scales=sc))),
+          run_oracle(inp, mode), mode, label=f"{mode} T={T} H={H} P={P} guarded")
+
+
+@pytest.mark.parametrize("kind", ["qk", "sharded", "mla"])
+def test_no_write_past_the_qk_family_outputs(fn, kind):
+    T, q, k = 300, 1536, (0 if kind == "sharded" else 520 if kind == "qk" else 512)
+    g = torch.Generator().manual_seed(5)
+    rows = torch.randn(T, q + k + 64, generator=g).to(torch.bfloat16).to(DEV)
+    wq = torch.ones(q, dtype=torch.bfloat16, device=DEV)
+    wk = torch.ones(max(k, 8), dtype=torch.bfloat16, device=DEV)[:k]
+    qb, qo = _guarded((T, q), torch.bfloat16, 3.0)
+    bufs = [qb]
+    if kind == "qk":
+        kb, ko = _guarded((T, k), torch.bfloat16, 3.0)
+        fn.qk_rmsnorm(rows, q, k, wq, wk, EPS, q_out=qo, k_out=ko)
+        bufs.append(kb)
+    elif kind == "sharded":
+        fn.sharded_rmsnorm(rows, wq, EPS, out=qo, H=q)
+    else:
+        yb, yo = _guarded((T, k), torch.bfloat16, 3.0)
+        cb, co = _guarded((T, q), torch.uint8, 0x5A)
+        sb, so = _guarded((T, q // 128), torch.float32, -7.0)
+        fn.ag_dual_rmsnorm(rows, q, k, wq, wk, quant=True, x_norm_out=qo, y_norm_out=yo,
+                           quant_out=co, scale_out=so)
+        bufs += [yb, cb, sb]
+    torch.cuda.synchronize()
+    for b in bufs:
+        tail = b[-GUARD:]
+        assert torch.all(tail == tail[0]) and float(tail[0]) in (3.0, 0x5A, -7.0), \
+            f"{kind}: an output's guard band was written"
