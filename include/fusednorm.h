@@ -175,6 +175,9 @@ int fused_add_rmsnorm_quant_fp8_static(const void* const* partials, int P,
  *   7 kRSAddResidualRMSNormFP8BlockWiseQuant as 6, with add_in
  *   8 kRSAddResidualRMSNorm                  as 1, with add_in
  * Patterns 0 (the bare collective) and 3, 5 (FP4) return FUSEDNORM_ERR_UNSUPPORTED.
+ * Outputs a pattern does not write (quant_out and scale_out for 1 and 8,
+ * scale_out for 2 and 4) and scale_factor outside 2 and 4 are ignored and may be
+ * NULL; the bare reduce-scattered sum is not written.
  *
  *   partials      HOST array of P device pointers, each bf16 [token_num, H] with
  *                 token_num >= token_offset + T (the caller guarantees it)
