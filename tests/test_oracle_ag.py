@@ -72,3 +72,22 @@ def test_q_part_block_codes():
     best = np.abs(r[..., None] - table).min(-1)
     got = oracle.e4m3_decode(codes)
     assert np.all(np.abs(np.abs(r - got) - best) <= 1e-6 * np.maximum(np.abs(r), 1e-3))
+
+
+def test_hand_rows():
+    # x = y = +-1 everywhere, unit gammas: mean of squares 1 in both segments, so
+    # x_norm = x / sqrt(1 + x_eps) and y_norm = y / sqrt(1 + y_eps); with x_eps = 0
+    # every x group's amax is 1, its scale 1/448 and its codes +-448 = 0x7E / 0xFE.
+    T = 3
+    sign = np.where(np.arange(Q + KV + ROPE) % 3 == 0, -1.0, 1.0)
+    rows = np.tile(oracle.bf16_encode(sign), (T, 1))
+    rows[:, Q + KV:] = 0x7FC0
+    out = oracle.ag_dual_rmsnorm(rows, Q, KV, oracle.bf16_encode(np.ones(Q)),
+                                 oracle.bf16_encode(np.ones(KV)), 0.0, 0.25, quant=True,
+                                 want_pre=True)
+    np.testing.assert_array_equal(out["yx"], np.tile(sign[:Q], (T, 1)))
+    np.testing.assert_allclose(out["yy"], np.tile(sign[Q:Q + KV], (T, 1)) / np.sqrt(1.25),
+                               rtol=1e-15)
+    np.testing.assert_array_equal(out["scales"], np.float32(1 / 448))
+    np.testing.assert_array_equal(out["codes"], np.where(np.tile(sign[:Q], (T, 1)) > 0, 0x7E, 0xFE))
+    assert not out["near_tie"].any()
