@@ -21,9 +21,11 @@ roofline is the dominant kernel's (the per-token FP8 epilogue).
 ``next_rows`` times the further entry points (sharded-hidden RMSNorm post
 stage, static-scale FP8, reduce-scatter epilogue, MLA all-gather epilogue) one
 launch at a time, each right after a prefill launch that evicts the last-level
-cache, so every timed launch reads its inputs from HBM.
+cache, so every timed launch reads its inputs from HBM. ``hbm_ceiling`` is the
+library's plain streaming read and copy on the same GPU; ``latency_shapes`` the
+per-call time of the two cache-resident shapes (16 x 1024, 128 x 7168).
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu-baseline] [--no-next]
 """
 import argparse
 import hashlib
