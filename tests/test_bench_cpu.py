@@ -1,0 +1,59 @@
+"""bench.py's host-side logic, on the CPU: the one-GPU refusal, the traffic
+figure tied to the kernel source it was measured on, and the CPU baseline's
+fields."""
+import json
+import os
+import subprocess
+import sys
+import types
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import oracle  # noqa: E402
+from residual_add_rmsnorm_amd import workloads as wl  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    for args, env in ((["--gpus", "2"], {}), ([], {"WORLD_SIZE": "4"})):
+        r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args],
+                           env=dict(os.environ, **env), capture_output=True, text=True,
+                           timeout=120)
+        assert r.returncode == 2 and "one GPU only" in r.stderr
+        assert r.stdout == ""
+
+
+def test_traffic_is_reported_only_for_the_measured_source(tmp_path, monkeypatch):
+    src = tmp_path / "kernels.hip"
+    src.write_text("// kernel source\n")
+    traffic = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "KERNEL_SRC", str(src))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(traffic))
+    assert bench.measured_traffic() is None                      # no file
+    traffic.write_text(json.dumps({"kernel_source_sha256": bench.source_digest(),
+                                   "bytes_per_launch": 123}))
+    assert bench.measured_traffic() == 123
+    src.write_text("// changed\n")
+    assert bench.measured_traffic() is None                      # stale after a change
+
+
+def test_cpu_baseline_fields():
+    parts = []
+    for name in bench.STEP:
+        w = wl.WORKLOADS[name].with_tokens(16)
+        c = wl.make_inputs(w)
+        var = None
+        if w.tp_world > 1:
+            rows = [wl.bits(c.qkv)] + [wl.bits(s) for s in c.shards]
+            var = torch.from_numpy(sum(oracle.qk_means(r, w.q_size, w.kv_size)
+                                       for r in rows).astype(np.float32))
+        parts.append(types.SimpleNamespace(name=name, w=w, cpu=c, var_in=var,
+                                           bytes=w.algorithmic_bytes()))
+    cb = bench.cpu_baseline(parts, min_seconds=0.0, max_reps=2)
+    assert set(cb) == {"value", "unit", "cores", "kind", "sample"}
+    assert cb["unit"] == "GB/s" and cb["kind"] == "oracle" and cb["value"] > 0
+    assert cb["cores"] == oracle.max_threads()
