@@ -1,11 +1,14 @@
-// Device code of libfusednorm: the fused tensor-parallel epilogue
+// Device code of libfusednorm, for gfx950: the fused tensor-parallel epilogue
 // (sum of P partial buffers + residual + RMSNorm, optionally OCP e4m3 with a
-// per-token or per-1x128-group scale) and the MiniMax QK RMSNorm, for gfx950.
+// per-token, per-1x128-group or static scale; also the reduce-scatter form
+// with an extra addend) and the RMSNorms over row segments: the MiniMax QK
+// norm, its one-segment (hidden-sharded) form and the MLA all-gather epilogue.
 //
 // What is computed follows the tokenspeed triton.py page, section "AMD Triton
 // All-Reduce + RMSNorm" (amd_allreduce_residual_rmsnorm_kernel), the fusion
-// patterns named in the tokenspeed trtllm.py page, section "Pattern enums",
-// and the vLLM minimax_rms_norm/rms_norm_tp page (_minimax_qk_var_kernel,
+// patterns named in the tokenspeed trtllm.py page, sections "Pattern enums",
+// "AllReduce fusion", "AllGather fusion" and "ReduceScatter fusion", and the
+// vLLM minimax_rms_norm/rms_norm_tp page (_minimax_qk_var_kernel,
 // _minimax_rms_apply_kernel). How it is computed is designed for CDNA4:
 //
 //   * the grid: one workgroup per token, the hardware dispatcher keeping every
