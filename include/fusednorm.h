@@ -43,17 +43,32 @@
  *     rejected with FUSEDNORM_ERR_UNSUPPORTED.
  *   - NaN or Inf inputs are outside the contract. With eps == 0 an all-zero
  *     token has no defined norm (0 * rsqrt(0)) and its outputs are NaN.
+ *
+ * Besides the entry points of the method, the library exports three
+ * measurement aids (fusednorm_stream_read / _copy / _mix, at the end of this
+ * file): plain streaming kernels that measure what HBM delivers for a given
+ * read/write mix, reported next to the epilogues' bandwidth. They compute
+ * nothing of the method.
  */
 #ifndef FUSEDNORM_H
 #define FUSEDNORM_H
 
 #include <stdint.h>
 
+/* The functions declared below are the library's whole dynamic interface: it
+ * is built with hidden default visibility, and this macro exports exactly
+ * them. */
+#if defined(__GNUC__) || defined(__clang__)
+#define FUSEDNORM_API __attribute__((visibility("default")))
+#else
+#define FUSEDNORM_API
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define FUSEDNORM_VERSION 10000 /* major*10000 + minor*100 + patch */
+#define FUSEDNORM_VERSION 10100 /* major*10000 + minor*100 + patch */
 #define FUSEDNORM_MAX_PARTIALS 16
 #define FUSEDNORM_MAX_HIDDEN 16384
 #define FUSEDNORM_FP8_GROUP 128
@@ -97,9 +112,9 @@ typedef enum {
  *   stream        hipStream_t or NULL
  * Returns a fusednorm_status.
  */
-int fused_add_rmsnorm(const void* const* partials, int P, const void* residual_in,
-                      const void* weight, int64_t T, int64_t H, float eps,
-                      void* norm_out, void* residual_out, void* stream);
+FUSEDNORM_API int fused_add_rmsnorm(const void* const* partials, int P, const void* residual_in,
+                                    const void* weight, int64_t T, int64_t H, float eps,
+                                    void* norm_out, void* residual_out, void* stream);
 
 /*
  * fused_add_rmsnorm_quant_fp8 -- pattern kARResidualRMSNormFP8Quant (with
@@ -118,10 +133,11 @@ int fused_add_rmsnorm(const void* const* partials, int P, const void* residual_i
  *   scale_out     fp32 [T], 4-B aligned, required
  * Other arguments as for fused_add_rmsnorm.
  */
-int fused_add_rmsnorm_quant_fp8(const void* const* partials, int P, const void* residual_in,
-                                const void* weight, int64_t T, int64_t H, float eps,
-                                void* norm_out, void* residual_out, void* quant_out,
-                                float* scale_out, void* stream);
+FUSEDNORM_API int fused_add_rmsnorm_quant_fp8(const void* const* partials, int P,
+                                              const void* residual_in, const void* weight,
+                                              int64_t T, int64_t H, float eps, void* norm_out,
+                                              void* residual_out, void* quant_out, float* scale_out,
+                                              void* stream);
 
 /*
  * fused_add_rmsnorm_quant_fp8_block -- pattern kARResidualRMSNormFP8BlockWiseQuant
@@ -136,11 +152,12 @@ int fused_add_rmsnorm_quant_fp8(const void* const* partials, int P, const void* 
  *   scale_out     fp32 [T, H/128] row-major, 4-B aligned, required
  * Other arguments as for fused_add_rmsnorm_quant_fp8.
  */
-int fused_add_rmsnorm_quant_fp8_block(const void* const* partials, int P,
-                                      const void* residual_in, const void* weight, int64_t T,
-                                      int64_t H, float eps, int group_size, void* norm_out,
-                                      void* residual_out, void* quant_out, float* scale_out,
-                                      void* stream);
+FUSEDNORM_API int fused_add_rmsnorm_quant_fp8_block(const void* const* partials, int P,
+                                                    const void* residual_in, const void* weight,
+                                                    int64_t T, int64_t H, float eps, int group_size,
+                                                    void* norm_out, void* residual_out,
+                                                    void* quant_out, float* scale_out,
+                                                    void* stream);
 
 /*
  * fused_add_rmsnorm_quant_fp8_static -- pattern kARResidualRMSNormFP8Quant with
@@ -155,11 +172,12 @@ int fused_add_rmsnorm_quant_fp8_block(const void* const* partials, int P,
  *   norm_out      bf16 [T, H] or NULL;  quant_out e4m3 [T, H], 16-B aligned
  * Other arguments as for fused_add_rmsnorm.
  */
-int fused_add_rmsnorm_quant_fp8_static(const void* const* partials, int P,
-                                       const void* residual_in, const void* weight, int64_t T,
-                                       int64_t H, float eps, const float* scale_factor,
-                                       void* norm_out, void* residual_out, void* quant_out,
-                                       void* stream);
+FUSEDNORM_API int fused_add_rmsnorm_quant_fp8_static(const void* const* partials, int P,
+                                                     const void* residual_in, const void* weight,
+                                                     int64_t T, int64_t H, float eps,
+                                                     const float* scale_factor, void* norm_out,
+                                                     void* residual_out, void* quant_out,
+                                                     void* stream);
 
 /*
  * fused_rs_epilogue -- the epilogue of a reduce-scatter fusion
@@ -187,10 +205,12 @@ int fused_add_rmsnorm_quant_fp8_static(const void* const* partials, int P,
  *                 fused_add_rmsnorm_quant_fp8_static), else ignored
  * Other arguments as for fused_add_rmsnorm and its FP8 variants.
  */
-int fused_rs_epilogue(int pattern, const void* const* partials, int P, int64_t token_offset,
-                      const void* add_in, const void* residual_in, const void* weight, int64_t T,
-                      int64_t H, float eps, const float* scale_factor, void* norm_out,
-                      void* residual_out, void* quant_out, float* scale_out, void* stream);
+FUSEDNORM_API int fused_rs_epilogue(int pattern, const void* const* partials, int P,
+                                    int64_t token_offset, const void* add_in,
+                                    const void* residual_in, const void* weight, int64_t T,
+                                    int64_t H, float eps, const float* scale_factor, void* norm_out,
+                                    void* residual_out, void* quant_out, float* scale_out,
+                                    void* stream);
 
 /*
  * ag_dual_rmsnorm -- the epilogue of the all-gather fusion for MLA on the
@@ -220,10 +240,11 @@ int fused_rs_epilogue(int pattern, const void* const* partials, int P, int64_t t
  *   quant_out     e4m3 [T, q_lora_rank], 8-B aligned
  *   scale_out     fp32 [T, q_lora_rank / 128], 4-B aligned
  */
-int ag_dual_rmsnorm(int pattern, const void* rows, int64_t T, int64_t row_stride,
-                    int64_t q_lora_rank, int64_t kv_lora_rank, const void* x_gamma,
-                    const void* y_gamma, float x_eps, float y_eps, void* x_norm_out,
-                    void* y_norm_out, void* quant_out, float* scale_out, void* stream);
+FUSEDNORM_API int ag_dual_rmsnorm(int pattern, const void* rows, int64_t T, int64_t row_stride,
+                                  int64_t q_lora_rank, int64_t kv_lora_rank, const void* x_gamma,
+                                  const void* y_gamma, float x_eps, float y_eps, void* x_norm_out,
+                                  void* y_norm_out, void* quant_out, float* scale_out,
+                                  void* stream);
 
 /*
  * qk_rmsnorm -- the MiniMax QK RMSNorm under tensor parallelism ([VLLM-QK]
@@ -251,9 +272,10 @@ int ag_dual_rmsnorm(int pattern, const void* rows, int64_t T, int64_t row_stride
  *   var_in        fp32 [T, 2], 8-B aligned, or NULL
  *   q_out         bf16 [T, q_size] contiguous;  k_out bf16 [T, kv_size] contiguous
  */
-int qk_rmsnorm(const void* qkv, int64_t T, int64_t row_stride, int64_t q_size,
-               int64_t kv_size, const void* q_weight, const void* k_weight, float eps,
-               int tp_world, const float* var_in, void* q_out, void* k_out, void* stream);
+FUSEDNORM_API int qk_rmsnorm(const void* qkv, int64_t T, int64_t row_stride, int64_t q_size,
+                             int64_t kv_size, const void* q_weight, const void* k_weight, float eps,
+                             int tp_world, const float* var_in, void* q_out, void* k_out,
+                             void* stream);
 
 /*
  * qk_rmsnorm_var -- the tensor-parallel "pre" stage of the QK norm ([VLLM-QK]
@@ -266,8 +288,8 @@ int qk_rmsnorm(const void* qkv, int64_t T, int64_t row_stride, int64_t q_size,
  *   var_out       fp32 [T, 2], 8-B aligned
  * Other arguments as for qk_rmsnorm.
  */
-int qk_rmsnorm_var(const void* qkv, int64_t T, int64_t row_stride, int64_t q_size,
-                   int64_t kv_size, float* var_out, void* stream);
+FUSEDNORM_API int qk_rmsnorm_var(const void* qkv, int64_t T, int64_t row_stride, int64_t q_size,
+                                 int64_t kv_size, float* var_out, void* stream);
 
 /*
  * sharded_rmsnorm -- RMSNorm of one matrix whose hidden dimension is split over
@@ -284,8 +306,9 @@ int qk_rmsnorm_var(const void* qkv, int64_t T, int64_t row_stride, int64_t q_siz
  *   weight        bf16 [H];  var_in fp32 [T], 4-B aligned, or NULL
  *   out           bf16 [T, H] contiguous
  */
-int sharded_rmsnorm(const void* x, int64_t T, int64_t row_stride, int64_t H, const void* weight,
-                    float eps, int tp_world, const float* var_in, void* out, void* stream);
+FUSEDNORM_API int sharded_rmsnorm(const void* x, int64_t T, int64_t row_stride, int64_t H,
+                                  const void* weight, float eps, int tp_world, const float* var_in,
+                                  void* out, void* stream);
 
 /*
  * sharded_rmsnorm_var -- the pre stage of sharded_rmsnorm ([VLLM-QK]
@@ -295,8 +318,8 @@ int sharded_rmsnorm(const void* x, int64_t T, int64_t row_stride, int64_t H, con
  *
  *   var_out       fp32 [T], 4-B aligned
  */
-int sharded_rmsnorm_var(const void* x, int64_t T, int64_t row_stride, int64_t H, float* var_out,
-                        void* stream);
+FUSEDNORM_API int sharded_rmsnorm_var(const void* x, int64_t T, int64_t row_stride, int64_t H,
+                                      float* var_out, void* stream);
 
 /*
  * fusednorm_e4m3_encode -- element-wise fp32 -> OCP E4M3 with exactly the
@@ -306,7 +329,7 @@ int sharded_rmsnorm_var(const void* x, int64_t T, int64_t row_stride, int64_t H,
  *
  *   in    fp32 [n], 16-B aligned;  out  uint8 [n], 16-B aligned;  n >= 0
  */
-int fusednorm_e4m3_encode(const float* in, void* out, int64_t n, void* stream);
+FUSEDNORM_API int fusednorm_e4m3_encode(const float* in, void* out, int64_t n, void* stream);
 
 /*
  * Measurement aids (not part of the method): plain streaming kernels that give
@@ -316,23 +339,46 @@ int fusednorm_e4m3_encode(const float* in, void* out, int64_t n, void* stream);
  *                          that no ordinary input reaches
  *   fusednorm_stream_copy  copies `bytes` from src to dst (no overlap)
  * bytes must be a positive multiple of 16 KiB; pointers 16-B aligned.
- * Returns FUSEDNORM_ERR_INVALID_ARGUMENT for NULL pointers or bytes <= 0,
- * FUSEDNORM_ERR_UNSUPPORTED for other unsupported sizes, alignment or overlap,
- * FUSEDNORM_ERR_HIP for a launch error. They do not set fusednorm_last_error.
+ *
+ *   fusednorm_stream_mix   the same bytes as one epilogue launch, moved with
+ *                          no arithmetic: for each of `rows` rows r it reads
+ *                          n_src source rows (source k: src_row_bytes bytes at
+ *                          src[k] + r * src_stride bytes) and writes n_dst
+ *                          destination rows (destination k: dst_row_bytes[k]
+ *                          bytes at dst[k] + r * dst_row_bytes[k]), each a
+ *                          byte mix of the sources (XOR of the first
+ *                          dst_row_bytes[k] bytes of every source row). One
+ *                          workgroup per row, 16-byte vectors, the source rows
+ *                          read two at a time, the row's stores issued together.
+ *                          src and dst are host arrays of device pointers.
+ *     1 <= n_src <= 16, 1 <= n_dst <= 4, rows >= 0 (0: nothing launched);
+ *     src_row_bytes a multiple of 16 in [16, 32768]; src_stride a multiple of
+ *     16, >= src_row_bytes; every dst_row_bytes[k] a multiple of 16 in
+ *     [16, src_row_bytes]; pointers 16-B aligned; no destination overlaps a
+ *     source or another destination.
+ *
+ * Returns FUSEDNORM_ERR_INVALID_ARGUMENT for NULL pointers, counts out of
+ * range or bytes <= 0, FUSEDNORM_ERR_UNSUPPORTED for other unsupported sizes,
+ * alignment or overlap, FUSEDNORM_ERR_HIP for a launch error. They do not set
+ * fusednorm_last_error.
  */
-int fusednorm_stream_read(const void* src, int64_t bytes, void* sink, void* stream);
-int fusednorm_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
+FUSEDNORM_API int fusednorm_stream_read(const void* src, int64_t bytes, void* sink, void* stream);
+FUSEDNORM_API int fusednorm_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
+FUSEDNORM_API int fusednorm_stream_mix(const void* const* src, int n_src, int64_t src_row_bytes,
+                                       int64_t src_stride, void* const* dst,
+                                       const int64_t* dst_row_bytes, int n_dst, int64_t rows,
+                                       void* stream);
 
 /* Static description of a status code. Never NULL. */
-const char* fusednorm_status_string(int status);
+FUSEDNORM_API const char* fusednorm_status_string(int status);
 
 /* Detail of the last non-OK status returned on the calling thread (which
  * argument failed which check); "" when there is none. Valid until the next
  * call on that thread. */
-const char* fusednorm_last_error(void);
+FUSEDNORM_API const char* fusednorm_last_error(void);
 
 /* FUSEDNORM_VERSION of the built library. */
-int fusednorm_version(void);
+FUSEDNORM_API int fusednorm_version(void);
 
 #ifdef __cplusplus
 }

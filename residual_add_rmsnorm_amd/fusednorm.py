@@ -67,6 +67,7 @@ def _load() -> ctypes.CDLL:
         "fusednorm_e4m3_encode": [vp, vp, i64, vp],
         "fusednorm_stream_read": [vp, i64, vp, vp],
         "fusednorm_stream_copy": [vp, vp, i64, vp],
+        "fusednorm_stream_mix": [vpp, i32, i64, i64, vpp, ctypes.POINTER(i64), i32, i64, vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -546,10 +547,41 @@ def stream_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
         raise FusedNormError("fusednorm_stream_copy", rc, "")
 
 
+def stream_mix(srcs: Sequence[torch.Tensor], dsts: Sequence[torch.Tensor], rows: int,
+               src_row_bytes: int, src_stride: Optional[int] = None, stream=None) -> None:
+    """Measurement aid: the bytes of one epilogue launch without its arithmetic.
+    For each of ``rows`` rows, reads ``src_row_bytes`` bytes of every source
+    (row r of source k at byte ``r * src_stride``, default ``src_row_bytes``)
+    and writes one row of every destination; destination k holds ``rows`` rows
+    of ``dsts[k].nbytes // rows`` bytes, contiguous."""
+    if rows <= 0:
+        raise ValueError("rows must be positive")
+    stride = src_row_bytes if src_stride is None else src_stride
+    for t in list(srcs) + list(dsts):
+        _need(t, "stream buffer", dtype=None)
+    _same_device([(f"stream buffer {k}", t) for k, t in enumerate(list(srcs) + list(dsts))],
+                 srcs[0].device)
+    for k, t in enumerate(srcs):
+        if t.nbytes < (rows - 1) * stride + src_row_bytes:
+            raise ValueError(f"source {k} holds fewer than {rows} rows")
+    widths = []
+    for k, t in enumerate(dsts):
+        if t.nbytes % rows:
+            raise ValueError(f"destination {k}: {t.nbytes} bytes is not a whole number of rows")
+        widths.append(t.nbytes // rows)
+    sp = (ctypes.c_void_p * len(srcs))(*[_ptr(t) for t in srcs])
+    dp = (ctypes.c_void_p * len(dsts))(*[_ptr(t) for t in dsts])
+    wb = (ctypes.c_int64 * len(dsts))(*widths)
+    rc = _lib.fusednorm_stream_mix(sp, len(srcs), src_row_bytes, stride, dp, wb, len(dsts), rows,
+                                   _stream(srcs[0].device, stream))
+    if rc != FUSEDNORM_OK:
+        raise FusedNormError("fusednorm_stream_mix", rc, "")
+
+
 __all__ = [
     "fused_add_rmsnorm", "fused_add_rmsnorm_quant_fp8", "fused_add_rmsnorm_quant_fp8_block",
     "fused_add_rmsnorm_quant_fp8_static", "fused_rs_epilogue", "ag_dual_rmsnorm",
     "qk_rmsnorm", "qk_rmsnorm_var", "sharded_rmsnorm", "sharded_rmsnorm_var", "e4m3_encode",
-    "stream_read", "stream_copy", "version", "library_path",
+    "stream_read", "stream_copy", "stream_mix", "version", "library_path",
     "FusedNormError", "FusedNormUnsupported", "FusedNormLibraryMissing",
 ]

@@ -37,8 +37,8 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return re.findall(r"^\s*(?:const\s+)?(?:int|char\s*\*|const char\s*\*)\s*\**\s*(\w+)\s*\(",
-                      text, re.M)
+    return re.findall(r"^\s*(?:FUSEDNORM_API\s+)?(?:const\s+)?(?:int|char\s*\*|const char\s*\*)"
+                      r"\s*\**\s*(\w+)\s*\(", text, re.M)
 
 
 def test_header_declares_the_entry_points():
@@ -50,14 +50,24 @@ def test_header_declares_the_entry_points():
             "fused_add_rmsnorm_quant_fp8_static", "fused_rs_epilogue", "ag_dual_rmsnorm"} <= names
 
 
-def test_library_exports_every_declared_symbol(lib):
+def test_library_exports_exactly_the_declared_functions(lib):
+    """The dynamic symbol table holds the header's functions and nothing else:
+    no internal C++ helper, no compiler data symbol."""
     out = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True,
                          text=True, check=True).stdout
-    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
-    missing = [n for n in declared_functions() if n not in exported]
-    assert not missing, missing
-    for n in declared_functions():
+    exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    declared = set(declared_functions())
+    assert exported == declared, (sorted(exported - declared), sorted(declared - exported))
+    for n in declared:
         assert getattr(lib, n) is not None
+
+
+def test_every_declaration_carries_the_export_macro():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    decls = re.findall(r"^(.*?)\b(\w+)\s*\([^;{]*\)\s*;", text, re.M)
+    assert decls
+    for prefix, name in decls:
+        assert prefix.startswith("FUSEDNORM_API "), name
 
 
 def test_version_and_status_strings(lib):
@@ -324,6 +334,34 @@ def test_stream_aid_validation(lib):
     assert cp(addr(1), None, K16, None) == 1
     assert cp(addr(1), addr(1, K16 // 2), K16, None) == 2      # overlapping
     assert cp(addr(1), addr(2, 4), K16, None) == 2
+
+
+def test_stream_mix_validation(lib):
+    mix = lib.fusednorm_stream_mix
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+
+    def call(srcs=(1, 2), dsts=(5,), widths=(1024,), row=1024, stride=None, rows=8):
+        sp = (vp * max(len(srcs), 1))(*[None if s is None else addr(s) for s in srcs])
+        dp = (vp * max(len(dsts), 1))(*[None if d is None else addr(d) for d in dsts])
+        wb = (i64 * max(len(widths), 1))(*widths)
+        return mix(sp, len(srcs), row, row if stride is None else stride, dp, wb, len(dsts),
+                   rows, None)
+
+    assert call(rows=0) == 0                                  # nothing to move
+    assert call(srcs=()) == 1
+    assert call(srcs=tuple(range(1, 18))) == 1                # 17 sources
+    assert call(dsts=(), widths=()) == 1
+    assert call(dsts=(5, 6, 7, 8, 9), widths=(16,) * 5) == 1
+    assert call(srcs=(1, None)) == 1
+    assert call(dsts=(None,)) == 1
+    assert call(rows=-1) == 1
+    assert call(widths=(0,)) == 1
+    assert call(row=1000, widths=(992,)) == 2                 # not a multiple of 16
+    assert call(row=32768 + 16, widths=(16,)) == 2            # row above 32 KiB
+    assert call(stride=512) == 2                              # stride below the row
+    assert call(widths=(2048,)) == 2                          # destination wider than the row
+    assert call(dsts=(1,)) == 2                               # destination over a source
+    assert call(dsts=(5, 5), widths=(1024, 1024)) == 2        # destinations overlap
 
 
 def test_c_client_compiles_as_c_and_runs(lib, tmp_path):
