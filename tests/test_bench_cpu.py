@@ -42,8 +42,8 @@ def test_traffic_is_reported_only_for_the_measured_source(tmp_path, monkeypatch)
 
 
 def test_cpu_baseline_fields():
-    parts = []
-    for name in bench.STEP:
+    runners = {}
+    for name in bench.STEP + bench.LATENCY:
         w = wl.WORKLOADS[name].with_tokens(16)
         c = wl.make_inputs(w)
         var = None
@@ -51,9 +51,29 @@ def test_cpu_baseline_fields():
             rows = [wl.bits(c.qkv)] + [wl.bits(s) for s in c.shards]
             var = torch.from_numpy(sum(oracle.qk_means(r, w.q_size, w.kv_size)
                                        for r in rows).astype(np.float32))
-        parts.append(types.SimpleNamespace(name=name, w=w, cpu=c, var_in=var,
-                                           bytes=w.algorithmic_bytes()))
-    cb = bench.cpu_baseline(parts, min_seconds=0.0, max_reps=2)
-    assert set(cb) == {"value", "unit", "cores", "kind", "sample"}
+        runners[name] = types.SimpleNamespace(name=name, w=w, cpu=c, var_in=var,
+                                              bytes=w.algorithmic_bytes())
+    threads = oracle.max_threads()
+    cb = bench.cpu_baseline(runners, min_seconds=0.0, max_reps=2)
+    assert set(cb) == {"value", "unit", "cores", "kind", "sample", "per_config"}
     assert cb["unit"] == "GB/s" and cb["kind"] == "oracle" and cb["value"] > 0
-    assert cb["cores"] == oracle.max_threads()
+    assert cb["cores"] == threads
+    assert set(cb["per_config"]) == set(bench.STEP + bench.LATENCY)
+    for name, rec in cb["per_config"].items():
+        assert rec["GB/s"] > 0 and rec["tokens/s"] > 0 and rec["threads"] == threads
+        assert ("one_thread" in rec) == (name in bench.LATENCY)
+    # the step figure is the step's bytes over the sum of its launches' times
+    step_s = sum(cb["per_config"][n]["s_per_launch"] for n in bench.STEP)
+    step_bytes = sum(runners[n].bytes for n in bench.STEP)
+    assert abs(cb["value"] - step_bytes / step_s / 1e9) <= 0.01 * cb["value"] + 1e-3
+    assert oracle.max_threads() == threads      # the one-thread leg restores the thread count
+
+
+def test_rotation_keeps_each_launch_out_of_the_last_level_cache():
+    for name in bench.STEP + bench.LATENCY + bench.NEXT:
+        w = wl.WORKLOADS[name]
+        k = bench.sets_for(w.algorithmic_bytes())
+        assert k * w.algorithmic_bytes() >= (1 << 30) or k == 128
+    assert bench.sets_for(wl.WORKLOADS["decode"].algorithmic_bytes()) == 84
+    assert bench.sets_for(wl.WORKLOADS["qk_local"].algorithmic_bytes()) == 10
+    assert bench.sets_for(wl.WORKLOADS["prefill_fp8_token"].algorithmic_bytes()) == 1
