@@ -12,9 +12,9 @@
 // _minimax_rms_apply_kernel). How it is computed is designed for CDNA4:
 //
 //   * the grid: one workgroup per token, the hardware dispatcher keeping every
-//     CU filled as workgroups finish; for the 7168-wide rows, two resident
-//     workgroups per CU, each looping over tokens and issuing the next token's
-//     loads as soon as the current token's sum is formed;
+//     CU filled as workgroups finish; for wide rows with few tokens per CU,
+//     two resident workgroups per CU, each looping over tokens and issuing the
+//     next token's loads as soon as the current token's sum is formed;
 //   * a token's row is cut into 16-byte vectors (8 bf16); vector i belongs to
 //     lane i mod blockDim, slot i / blockDim, so every wave-wide access covers
 //     1 KiB of consecutive bytes, read and written through per-row buffer
@@ -695,15 +695,22 @@ LaunchShape pick_epilogue_shape(int nvec, int P, int64_t T, int cus) {
         }
         return LaunchShape{0, 0, 0, 0};
     }
-    // Many tokens. Measured on MI355X, inputs out of cache: one workgroup per
-    // token, 256 threads (fewer for rows of fewer than 256 vectors), partials
-    // two buffers at a time, was the fastest shape or within 1% of it for rows
-    // of 1024 to 16384 elements with 2 to 16 partials, 1.05x to 1.9x faster
-    // than two resident workgroups per CU looping over tokens. The exception is
-    // the 7168-wide rows: there two resident 448-thread workgroups per CU with
-    // next-token prefetch ran 6% faster inside the benchmark step (block FP8,
-    // 2 partials), as fast for 4 and 9 partials.
-    if (nvec == 896) return LaunchShape{2, 448, 2, 2};
+    // Many tokens: 256 threads (fewer for rows of fewer than 256 vectors),
+    // partials two buffers at a time. Measured on MI355X, inputs out of cache,
+    // rows of 2048 to 8192 elements with 2 and 8 partials: for rows of at
+    // least 14 KiB (896 vectors) and at most 8 tokens per CU, two resident
+    // workgroups per CU that loop over tokens and prefetch the next token's
+    // loads were up to 8% faster (the ramp-up and the tail are a large share
+    // of such a launch), and with 8 or more partials two vectors per lane on
+    // half-row-wide workgroups were 1% to 3% faster again; with more tokens
+    // per CU, or narrower rows, one workgroup per token was 3% to 20% faster.
+    if (nvec >= 896 && T <= 8 * (int64_t)cus) {
+        if (P >= 8 && nvec % 128 == 0 && nvec / 2 <= max_threads_for(2, 2))
+            return LaunchShape{2, nvec / 2, 2, 2};
+        const int vpt = (nvec + 255) / 256;
+        if (vpt > kMaxVpt) return LaunchShape{0, 0, 0, 0};
+        return LaunchShape{vpt, 256, 2, 2};
+    }
     const int threads = round_up_wave(nvec < 256 ? nvec : 256);
     const int vpt = (nvec + threads - 1) / threads;
     if (vpt > kMaxVpt) return LaunchShape{0, 0, 0, 0};

@@ -355,9 +355,10 @@ def test_qk_empty_and_invalid(fn):
 @pytest.mark.parametrize("H,P", [(8, 1), (1024, 3), (4104, 8), (7168, 2), (8192, 8), (16384, 16),
                                  (1152, 5), (2048, 12)])
 def test_many_tokens_per_workgroup(fn, mode, H, P):
-    """T well above the number of CUs. The 7168-wide rows run on two resident
+    """T well above the number of CUs (700 or 1100 tokens, at most 8 per CU):
+    rows of at least 14 KiB (7168, 8192, 16384 wide) run on two resident
     workgroups per CU that loop over tokens and prefetch across them; the
-    others run one workgroup per token."""
+    narrower rows run one workgroup per token."""
     if mode == "quant_block" and H % 128:
         pytest.skip("block FP8 needs H % 128 == 0")
     T = 1100 if H <= 8192 else 700
@@ -491,8 +492,8 @@ def test_graph_capture_replays_match_eager(fn):
 
 
 def test_graph_capture_further_entry_points(fn):
-    """The sharded stages, static-scale FP8, the reduce-scatter epilogue (on
-    the persistent 7168-wide grid) and the MLA epilogue captured in one HIP
+    """The sharded stages, static-scale FP8 and the reduce-scatter epilogue
+    (both on the persistent grid of wide rows) and the MLA epilogue captured in one HIP
     graph: every replay, between eager runs, equals the eager result."""
     g_ = torch.Generator().manual_seed(21)
     x = torch.randn(700, 2048, generator=g_).to(torch.bfloat16).to(DEV)
@@ -780,8 +781,9 @@ print("ok", flush=True)
 
 
 def test_first_call_inside_a_graph_capture():
-    """A process whose first library call is captured (the persistent 7168-wide
-    grid queries the kernel's occupancy on first use) replays correctly."""
+    """A process whose first library call is captured (the persistent grid,
+    here 600 tokens of 7168, queries the kernel's occupancy on first use)
+    replays correctly."""
     import subprocess
     import sys
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
