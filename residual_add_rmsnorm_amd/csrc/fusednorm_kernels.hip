@@ -405,8 +405,9 @@ fused_epilogue_kernel(EpilogueArgs a, int64_t T) {
                 group_max = row16_reduce(group_max, Max{});
                 q = quant_scale(group_max);
             }
-            // lanes past the end of the row (valid[s] false) are dropped by the
-            // resources' range check
+            // lanes past the end of the row (valid[s] false) issue no stores
+            // (the group maximum above still takes every lane of the DPP row)
+            if (!valid[s]) continue;
             store16(out_res, off[s], pack_bf16x8(x[s]));
             if (a.norm_out) {
                 float y[8];
@@ -426,7 +427,7 @@ fused_epilogue_kernel(EpilogueArgs a, int64_t T) {
                 u32x2 codes = pack_e4m3x8(r);
                 if (q.qmul == 0.0f) codes = u32x2{0u, 0u};  // all-zero token or group: +0 codes
                 store8(out_q, off[s] / 2u, codes);
-                if (MODE == kModeQuantBlock && valid[s] && (tid & 15) == 0)
+                if (MODE == kModeQuantBlock && (tid & 15) == 0)
                     a.scale_out[t * a.groups + i / 16] = (group_max * inv) / 448.0f;
             }
         }
@@ -502,13 +503,14 @@ __global__ void __launch_bounds__(max_threads_for(VPT)) qk_norm_kernel(QkArgs a,
             const float inv_q = rsqrtf(var_q / a.tp_world + a.eps);
             const float inv_k = rsqrtf(var_k / a.tp_world + a.eps_k);
             // a null q_out (quantised q only) and the k output of one segment
-            // get resources of zero bytes: every store to them is dropped
+            // get resources of zero bytes, and are never stored to
             const Row out_q = a.q_out ? make_row(a.q_out + t * a.nq, (uint32_t)a.nq * 16u)
                                       : make_row(a.k_out, 0u);
             const Row out_k = seg == 2 ? make_row(a.k_out + t * a.nk, (uint32_t)a.nk * 16u)
                                        : make_row(a.q_out, 0u);
             const Row out_c = MODE == kQkQuant ? make_row(a.quant_out + t * a.nq, (uint32_t)a.nq * 8u)
                                                : out_k;
+            const bool want_q = a.q_out != nullptr;
 #pragma unroll
             for (int s = 0; s < VPT; ++s) {
                 const float inv = is_q[s] ? inv_q : inv_k;
@@ -517,11 +519,14 @@ __global__ void __launch_bounds__(max_threads_for(VPT)) qk_norm_kernel(QkArgs a,
                 unpack8(wv[s], w);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) y[e] = (f[e] * inv) * w[e];
-                // a k vector's offset within q_out is past its end, and a q
-                // vector's offset within k_out wraps past k_out's end: the range
-                // check drops the store that does not apply
-                store16(out_q, off[s], pack_bf16x8(y));
-                store16(out_k, off[s] - (uint32_t)a.nq * 16u, pack_bf16x8(y));
+                // each lane issues only the store that applies to its vector
+                // (a wave's vectors are all q or all k except at the one wave
+                // that straddles the boundary, so the branch rarely diverges)
+                if (is_q[s]) {
+                    if (want_q) store16(out_q, off[s], pack_bf16x8(y));
+                } else if (valid[s]) {
+                    store16(out_k, off[s] - (uint32_t)a.nq * 16u, pack_bf16x8(y));
+                }
                 if (MODE == kQkQuant) {
                     // A 1x128 group is the 16 lanes of one DPP row in one slot;
                     // q_size is a multiple of 128, so no group reaches into k.
@@ -540,7 +545,7 @@ __global__ void __launch_bounds__(max_threads_for(VPT)) qk_norm_kernel(QkArgs a,
                     for (int e = 0; e < 8; ++e) r[e] = (xw[e] * q.pre) * q.qmul;
                     u32x2 codes = pack_e4m3x8(r);
                     if (q.qmul == 0.0f) codes = u32x2{0u, 0u};  // all-zero group: +0 codes
-                    store8(out_c, off[s] / 2u, codes);       // k vectors: past the end, dropped
+                    if (is_q[s]) store8(out_c, off[s] / 2u, codes);
                     const int i = s * nthr + tid;
                     if (is_q[s] && (tid & 15) == 0)
                         a.scale_out[t * a.groups + i / 16] = (gmax * inv_q) / 448.0f;

@@ -50,9 +50,9 @@ __global__ void __launch_bounds__(kThreads) stream_copy_kernel(const u32x4* __re
 // per row (grid-stride past 2^20 rows); lane l owns the row's 16-byte vectors
 // l, l + 256, ... (VPT of them), so every wave access is 1 KiB of consecutive
 // bytes; two source rows are in flight at a time. The row's destination
-// stores are issued together after a workgroup barrier. All accesses go
-// through buffer resources sized to the row, so lanes past a row's end read
-// zeros and their stores are dropped.
+// stores are issued together after a workgroup barrier, each lane storing only
+// within each destination row. All accesses go through buffer resources sized
+// to the row, so lanes past a row's end read zeros.
 constexpr int kMixMaxSrc = 16;
 constexpr int kMixMaxDst = 4;
 constexpr int kMixThreads = 256;
@@ -107,7 +107,9 @@ __global__ void __launch_bounds__(kMixThreads) stream_mix_kernel(MixArgs a, int6
             const __amdgpu_buffer_rsrc_t rs =
                 mix_row(a.dst[d] + r * (a.dst_bytes[d] / 16u), a.dst_bytes[d]);
 #pragma unroll
-            for (int s = 0; s < VPT; ++s) __builtin_amdgcn_raw_buffer_store_b128(acc[s], rs, off[s], 0, 2);
+            for (int s = 0; s < VPT; ++s)
+                if (off[s] < a.dst_bytes[d])  // lanes past the destination row issue no store
+                    __builtin_amdgcn_raw_buffer_store_b128(acc[s], rs, off[s], 0, 2);
         }
     }
 }
