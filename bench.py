@@ -36,8 +36,13 @@ Prints ONE JSON line:
                       latency shapes on one thread.
   next_rows           the further entry points, each timed alone like
                       per_config.
+  token_sweep         the QK norm (local means) and the MLA epilogue at 1024 to
+                      32768 tokens, timed like per_config, with the least-
+                      squares fit us = fixed_us + bytes / (stream_GBs * 1e3):
+                      the fixed cost of a launch and its streaming rate.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu-baseline] [--no-next]
+                    [--no-sweep]
 """
 import argparse
 import hashlib
@@ -60,6 +65,9 @@ LATENCY = ["tiny", "decode"]
 DOMINANT = "prefill_fp8_token"
 # Entry points beyond the step, each timed alone on its own workload.
 NEXT = ["sharded_post", "static_fp8", "rs_fp8_block", "mla_ag_fp8"]
+# Workloads timed over token counts for the fixed-cost fit.
+SWEEP = ["qk_local", "mla_ag_fp8"]
+SWEEP_TOKENS = [1024, 2048, 4096, 8192, 16384, 32768]
 
 
 def log(*a):
@@ -75,6 +83,8 @@ def parse():
                     help="skip the CPU oracle leg (for profiler runs)")
     ap.add_argument("--no-next", action="store_true",
                     help="skip timing the entry points beyond the step")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the token-count sweep of the QK norm and the MLA epilogue")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
     return ap.parse_args()
 
@@ -108,9 +118,9 @@ class Runner:
     launch i using copy i % sets; `call(i)` is the entry point, `mix(i)` the
     library's mixed-stream kernel over the same sources and destinations."""
 
-    def __init__(self, name, fn, wl, torch, dev):
+    def __init__(self, name, fn, wl, torch, dev, T=None, quiet=False):
         self.name = name
-        self.w = w = wl.WORKLOADS[name]
+        self.w = w = wl.WORKLOADS[name] if T is None else wl.WORKLOADS[name].with_tokens(T)
         t0 = time.perf_counter()
         self.cpu = wl.make_inputs(w)
         self.bytes = w.algorithmic_bytes()
@@ -221,9 +231,10 @@ class Runner:
         srcs, dsts_, row, _ = self._mix(S[0])
         self.mix_bytes = w.T * (len(srcs) * row + sum(d.nbytes // w.T for d in dsts_))
         self.fn = fn
-        log(f"[bench] {name}: {w.description}; {self.bytes / 1e6:.1f} MB per launch, "
-            f"{self.sets} resident cop{'y' if self.sets == 1 else 'ies'} "
-            f"(inputs drawn in {time.perf_counter() - t0:.1f} s)")
+        if not quiet:
+            log(f"[bench] {name}: {w.description}; {self.bytes / 1e6:.1f} MB per launch, "
+                f"{self.sets} resident cop{'y' if self.sets == 1 else 'ies'} "
+                f"(inputs drawn in {time.perf_counter() - t0:.1f} s)")
 
     def call(self, i=0):
         return self._call(self.S[i % self.sets])
@@ -285,6 +296,39 @@ def measure(r, torch, launches=50):
         f"{HBM_PEAK_GBS:.0f}); same bytes, no arithmetic: {mix_us:.2f} us, {mix_gbs:.1f} GB/s; "
         f"{100 * gbs / mix_gbs:.1f}% of that{' (cache-resident)' if r.cache_resident else ''}")
     return out
+
+
+def token_sweep(fn, wl, torch, dev):
+    """Each SWEEP workload at every SWEEP_TOKENS count, timed like per_config
+    (rotating resident copies, N launches in a graph), and the least-squares
+    line through (bytes, us): the intercept is the launch's fixed cost, the
+    slope the rate at which it streams its bytes."""
+    out = {}
+    for name in SWEEP:
+        pts = []
+        for T in SWEEP_TOKENS:
+            r = Runner(name, fn, wl, torch, dev, T=T, quiet=True)
+            n = r.sets * math.ceil(10 / r.sets)
+            us = time_launches(torch, r.call, n, math.ceil(50 / n))
+            pts.append({"T": T, "bytes": r.bytes, "resident_copies": r.sets, "us": round(us, 2),
+                        "GB/s": round(r.bytes / us / 1e3, 1)})
+            del r
+            torch.cuda.empty_cache()
+        fixed, rate = fit_fixed_and_rate([p["bytes"] for p in pts], [p["us"] for p in pts])
+        out[name] = {"points": pts, "fixed_us": round(fixed, 2), "stream_GBs": round(rate, 1)}
+        log(f"[bench] {name} over {SWEEP_TOKENS[0]}..{SWEEP_TOKENS[-1]} tokens: "
+            f"{fixed:.2f} us fixed + bytes at {rate:.1f} GB/s")
+    return out
+
+
+def fit_fixed_and_rate(nbytes, us):
+    """Least-squares line us = fixed + nbytes / (rate * 1e3): returns (fixed
+    in us, rate in GB/s)."""
+    n = len(nbytes)
+    mx, my = sum(nbytes) / n, sum(us) / n
+    slope = sum((x - mx) * (y - my) for x, y in zip(nbytes, us)) / \
+        sum((x - mx) ** 2 for x in nbytes)
+    return my - slope * mx, 1.0 / slope / 1e3
 
 
 def ceilings(fn, torch, dev, reps=10):
@@ -484,6 +528,8 @@ def main():
             result["next_rows"][n] = measure(r, torch)
             del r
             torch.cuda.empty_cache()
+    if not args.no_sweep:
+        result["token_sweep"] = token_sweep(fn, wl, torch, dev)
     line = json.dumps(result)
     if args.out:
         with open(args.out, "w") as f:

@@ -2,7 +2,14 @@
 
 Rules (the tolerances the fused epilogue is held to):
   * bf16: at most ``max_ulp`` (1) units in the last place apart, measured on
-    the ordered bf16 bit patterns (so +0 and -0 are the same point);
+    the ordered bf16 bit patterns (so +0 and -0 are the same point); given the
+    oracle's unrounded value as well, a value one unit away must be the other
+    bf16 neighbour of that exact value (the two bracket it), and every value
+    must lie within 2^-8 of the exact value, relative, plus 2^-16 for the
+    kernel's own fp32 roundings (where the exact value is a normal bf16
+    number): the correctly rounded value is within half a unit, 2^-8, and the
+    kernel's fp32 arithmetic can only pick the other neighbour of an exact
+    value that lies next to the midpoint between the two;
   * fp32 scales: relative difference at most 1e-6 (both exactly 0 for zero
     rows);
   * e4m3 codes: identical, except (i) codes of the same sign one step apart
@@ -32,17 +39,24 @@ class Bf16Report:
     n: int
     n_diff: int          # elements not bit-identical (after +0/-0 folding)
     max_ulp: int
-    max_rel: float
+    max_rel: float       # against the oracle's rounded bf16 value
+    max_rel_exact: float = float("nan")   # against the oracle's unrounded value, if given
 
     def __str__(self):
+        ex = "" if self.max_rel_exact != self.max_rel_exact else \
+            f", max rel to the exact value {self.max_rel_exact:.3g}"
         if self.n_diff == 0:
-            return f"bf16: {self.n} values, all bit-identical"
+            return f"bf16: {self.n} values, all bit-identical{ex}"
         return (f"bf16: {self.n} values, {self.n_diff} differ by <= {self.max_ulp} ulp, "
-                f"max rel {self.max_rel:.3g}")
+                f"max rel {self.max_rel:.3g}{ex}")
 
 
-def compare_bf16(got: np.ndarray, want: np.ndarray, max_ulp: int = 1, what: str = "bf16"
-                 ) -> Bf16Report:
+REL_EXACT = 2.0 ** -8 + 2.0 ** -16
+SMALLEST_NORMAL = 2.0 ** -126
+
+
+def compare_bf16(got: np.ndarray, want: np.ndarray, max_ulp: int = 1, what: str = "bf16",
+                 exact: np.ndarray = None, rtol_exact: float = REL_EXACT) -> Bf16Report:
     got = np.asarray(got, np.uint16).reshape(-1)
     want = np.asarray(want, np.uint16).reshape(-1)
     assert got.shape == want.shape, f"{what}: shape {got.shape} vs {want.shape}"
@@ -63,8 +77,32 @@ def compare_bf16(got: np.ndarray, want: np.ndarray, max_ulp: int = 1, what: str 
     wf = (want[ok].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     with np.errstate(divide="ignore", invalid="ignore"):
         rel = np.where(wf != 0, np.abs(gf - wf) / np.abs(wf), np.abs(gf))
+    rel_exact = float("nan")
+    if exact is not None:
+        ex = np.asarray(exact, np.float64).reshape(-1)
+        assert ex.shape == got.shape, f"{what}: exact shape {ex.shape} vs {got.shape}"
+        ex = ex[ok]
+        # a value one unit from the correctly rounded one must lie on the other
+        # side of the exact value: the two bf16 values bracket it
+        step = _bf16_order(got[ok]) - _bf16_order(want[ok])
+        side = np.sign(ex - wf)
+        wrong = (step != 0) & (step != side)
+        if wrong.any():
+            i = np.nonzero(ok)[0][int(np.nonzero(wrong)[0][0])]
+            raise AssertionError(f"{what}: at flat index {i} got {got[i]:#06x}, which with "
+                                 f"{want[i]:#06x} does not bracket the exact value "
+                                 f"{float(np.asarray(exact).reshape(-1)[i])!r}")
+        with np.errstate(divide="ignore", invalid="ignore"):
+            re = np.where(ex != 0, np.abs(gf - ex) / np.abs(ex), np.abs(gf))
+        normal = np.abs(ex) >= SMALLEST_NORMAL
+        if np.any(re[normal] > rtol_exact):
+            j = int(np.argmax(np.where(normal, re, 0.0)))
+            i = np.nonzero(ok)[0][j]
+            raise AssertionError(f"{what}: at flat index {i} got {got[i]:#06x}, {re[j]:.3g} "
+                                 f"from the exact value {ex[j]!r} (bound {rtol_exact:.4g})")
+        rel_exact = float(re[normal].max()) if normal.any() else 0.0
     return Bf16Report(int(got.size), int((d > 0).sum()), worst,
-                      float(rel.max()) if rel.size else 0.0)
+                      float(rel.max()) if rel.size else 0.0, rel_exact)
 
 
 def compare_scales(got: np.ndarray, want: np.ndarray, rtol: float = 1e-6, what: str = "scale"

@@ -77,3 +77,10 @@ def test_rotation_keeps_each_launch_out_of_the_last_level_cache():
     assert bench.sets_for(wl.WORKLOADS["decode"].algorithmic_bytes()) == 84
     assert bench.sets_for(wl.WORKLOADS["qk_local"].algorithmic_bytes()) == 10
     assert bench.sets_for(wl.WORKLOADS["prefill_fp8_token"].algorithmic_bytes()) == 1
+
+
+def test_fixed_cost_fit_recovers_a_known_line():
+    nbytes = [29e6, 59e6, 117e6, 235e6, 470e6, 940e6]
+    us = [2.4 + b / 6.2e6 for b in nbytes]       # 2.4 us + bytes at 6.2 TB/s (6.2e6 B per us)
+    fixed, rate = bench.fit_fixed_and_rate(nbytes, us)
+    assert abs(fixed - 2.4) < 1e-9 and abs(rate - 6200.0) < 1e-6

@@ -66,14 +66,18 @@ def run_gpu(fn, inp, mode, want_norm=True, inplace=False):
     return dict(norm=norm, residual=rout, codes=q, scales=s)
 
 
-def run_oracle(inp, mode, want_norm=True, rows=None):
+def run_oracle(inp, mode, want_norm=True, rows=None, want_pre=None):
+    """The oracle on the same inputs; with the unrounded normalised values
+    whenever norm_out is compared (want_pre None)."""
+    if want_pre is None:
+        want_pre = mode == "norm" or want_norm
     parts = [wl.bits(p) for p in inp.partials]
     res = wl.bits(inp.residual)
     if rows is not None:
         parts = [np.ascontiguousarray(p[rows]) for p in parts]
         res = np.ascontiguousarray(res[rows])
     return oracle.fused_add_rmsnorm(parts, res, wl.bits(inp.weight), inp.workload.eps,
-                                    quant=MODES[mode], want_norm=want_norm)
+                                    quant=MODES[mode], want_norm=want_norm, want_pre=want_pre)
 
 
 def check(gpu, ref, mode, want_norm=True, rows=None, label=""):
@@ -83,7 +87,9 @@ def check(gpu, ref, mode, want_norm=True, rows=None, label=""):
     rep = [label]
     compare_bf16(g("residual", u16), ref["residual"], max_ulp=0, what="residual_out")
     if mode == "norm" or want_norm:
-        rep.append(str(compare_bf16(g("norm", u16), ref["norm"], what="norm_out")))
+        # with the oracle's unrounded y, a value one unit off must bracket it
+        rep.append(str(compare_bf16(g("norm", u16), ref["norm"], what="norm_out",
+                                    exact=ref.get("y") if rows is None else None)))
     if mode != "norm":
         rep.append(str(compare_e4m3(g("codes", u8), ref["codes"], ref["near_tie"])))
         sc = gpu["scales"].cpu().numpy()
@@ -147,9 +153,9 @@ def test_workload_qk_full(fn, name):
                          None if var_in is None else torch.from_numpy(var_in).to(DEV))
     torch.cuda.synchronize()
     ref = oracle.qk_rmsnorm(qkv_b, w.q_size, w.kv_size, wl.bits(inp.q_weight),
-                            wl.bits(inp.k_weight), w.eps, w.tp_world, var_in)
-    say(name, compare_bf16(u16(q), ref["q"], what="q_out"),
-        compare_bf16(u16(k), ref["k"], what="k_out"))
+                            wl.bits(inp.k_weight), w.eps, w.tp_world, var_in, want_pre=True)
+    say(name, compare_bf16(u16(q), ref["q"], what="q_out", exact=ref["yq"]),
+        compare_bf16(u16(k), ref["k"], what="k_out", exact=ref["yk"]))
 
 
 # ----------------------------------------------------------------------------- sweeps
