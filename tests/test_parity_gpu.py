@@ -372,6 +372,23 @@ def test_many_tokens_per_workgroup(fn, mode, H, P):
     check(run_gpu(fn, inp, mode), run_oracle(inp, mode), mode, label=f"{mode} T={T} H={H} P={P}")
 
 
+def _cus():
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+@pytest.mark.parametrize("H,P", [(7168, 2), (8192, 9), (4096, 3)])
+@pytest.mark.parametrize("where", ["cus", "cus+1", "8cus", "8cus+1"])
+def test_launch_policy_boundaries(fn, mode, H, P, where):
+    """Token counts on both sides of the launch rule's boundaries (as many
+    tokens as CUs; 8 tokens per CU, up to which wide rows take the persistent
+    grid): the grid decides only speed, every shape computes the same result."""
+    n = _cus()
+    T = {"cus": n, "cus+1": n + 1, "8cus": 8 * n, "8cus+1": 8 * n + 1}[where]
+    inp = norm_case(T, H, P, mode, outliers=0.002, seed=T + H + P)
+    check(run_gpu(fn, inp, mode), run_oracle(inp, mode), mode, label=f"{mode} T={T} H={H} P={P}")
+
+
 @pytest.mark.parametrize("mode", ["norm", "quant_token"])
 def test_grid_stride_past_the_grid_limit(fn, mode):
     """More tokens than the largest grid (2^20 workgroups): the first 37
