@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfusednorm.so")
 SOURCES = [os.path.join(CSRC, "fusednorm_kernels.hip"), os.path.join(CSRC, "fusednorm_api.cpp"),
-           os.path.join(CSRC, "fusednorm_stream.hip")]
+           os.path.join(CSRC, "fusednorm_launch_policy.cpp"), os.path.join(CSRC, "fusednorm_stream.hip")]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
