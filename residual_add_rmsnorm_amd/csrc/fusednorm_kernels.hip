@@ -19,7 +19,8 @@
 //     lane i mod blockDim, slot i / blockDim, so every wave-wide access covers
 //     1 KiB of consecutive bytes, read and written through per-row buffer
 //     resources with the non-temporal policy (lanes past the row end read
-//     zeros and their stores are dropped by the hardware range check);
+//     zeros and issue no stores; the hardware range check of the resources
+//     bounds every access to its row);
 //   * the fp32 row stays in VGPRs between the reduction and the normalisation;
 //     sums and maxima are reduced inside a wave with DPP row permutes plus two
 //     cross-row lane shuffles, then across the token's waves through LDS;
