@@ -18,6 +18,9 @@
 #include "fusednorm.h"
 #include "fusednorm_internal.h"
 
+static_assert(FUSEDNORM_MAX_HIDDEN / FUSEDNORM_FP8_GROUP <= fusednorm::kMaxGroups,
+              "the kernels gather a row's 1x128 scales in a fixed LDS array");
+
 namespace {
 
 using fusednorm::u32x2;

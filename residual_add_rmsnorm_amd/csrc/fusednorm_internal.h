@@ -14,6 +14,7 @@ constexpr int kWave = 64;
 constexpr int kMaxWaves = 16;   // 1024 threads per workgroup
 constexpr int kMaxPartials = 16;
 constexpr int kMaxVpt = 8;      // 16-byte vectors per lane per token
+constexpr int kMaxGroups = 128;  // 1x128 FP8 groups in the widest row (16384)
 // The fused epilogue keeps CH*VPT prefetched 16-byte vectors per lane (CH =
 // partial buffers loaded together); beyond this the kernel would spill.
 constexpr int kMaxLoadsPerLane = 16;

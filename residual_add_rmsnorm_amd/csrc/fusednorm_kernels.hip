@@ -25,7 +25,12 @@
 //     sums and maxima are reduced inside a wave with DPP row permutes plus two
 //     cross-row lane shuffles, then across the token's waves through LDS;
 //   * a 1x128 FP8 group is 16 consecutive vectors = 16 consecutive lanes of
-//     one wave = one DPP row, so a group's amax needs no LDS;
+//     one wave = one DPP row, so a group's amax needs no LDS; in the fused
+//     epilogue the amaxes go to LDS before the token's reduction barrier and
+//     the token's scale row is stored after it by one instruction, one lane
+//     per group (16 bytes from each wave at different times, into cache lines
+//     shared with neighbouring tokens' rows written from other XCDs, measured
+//     1.3% slower on the 16384 x 7168 launch);
 //   * stores are 16-byte (bf16) and 8-byte (e4m3) vectors made with gfx950's
 //     packed conversions v_cvt_pk_bf16_f32 and v_cvt_pk_fp8_f32.
 #include <hip/hip_runtime.h>
@@ -349,6 +354,10 @@ fused_epilogue_kernel(EpilogueArgs a, int64_t T) {
 
     // static FP8: one dequantisation scale s for the tensor; codes from y * (1/s)
     const float static_rcp = MODE == kModeQuantStatic ? 1.0f / *a.static_scale : 0.0f;
+    // block FP8: each group's max |x*w|, published by the reduction's barrier
+    // so that the token's scale row is stored by one instruction (two buffers:
+    // a token's maxima are written before its barrier, read after it)
+    __shared__ float row_gmax[2][MODE == kModeQuantBlock ? kMaxGroups : 1];
 
     int64_t t = blockIdx.x;  // the host launches at most T workgroups
     TokenLoads<VPT, CH> L;
@@ -361,22 +370,37 @@ fused_epilogue_kernel(EpilogueArgs a, int64_t T) {
         const bool more = t_next < T;
         if (more) issue_token_loads(a, n0, t_next * a.nvec, off, L);
 
-        // Token statistics: sum of x^2 and, for per-token FP8, max |x*w|.
+        // Token statistics: sum of x^2 and, for per-token FP8, max |x*w|; for
+        // block FP8 the max |x*w| of each 1x128 group (the 16 lanes of one DPP
+        // row in one slot; every lane takes part, lanes past the row hold 0).
         float part[VPT];
         float xw_max = 0.0f;
+        float group_max[VPT];
 #pragma unroll
         for (int s = 0; s < VPT; ++s) {
             part[s] = sumsq8(x[s]);
-            if (MODE == kModeQuantToken) {
+            if (MODE == kModeQuantToken || MODE == kModeQuantBlock) {
                 float w[8];
                 unpack8(wv[s], w);
+                float m = 0.0f;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) xw_max = fmaxf(xw_max, fabsf(x[s][e] * w[e]));
+                for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[s][e] * w[e]));
+                if (MODE == kModeQuantToken) xw_max = fmaxf(xw_max, m);
+                if (MODE == kModeQuantBlock) {
+                    group_max[s] = row16_reduce(m, Max{});
+                    if (valid[s] && (tid & 15) == 0) row_gmax[parity][(s * nthr + tid) / 16] = group_max[s];
+                }
             }
         }
         float ss = tree_sum(part);
         block_reduce<MODE == kModeQuantToken>(ss, xw_max, Max{}, parity);
         const float inv = rsqrtf(ss / a.h + a.eps);
+        // One contiguous store of the token's scale row. Written a few bytes
+        // per wave instead, pieces of a row whose cache lines it shares with
+        // neighbouring tokens' rows (written from other XCDs) cost time at the
+        // memory side.
+        if (MODE == kModeQuantBlock && tid < a.groups)
+            a.scale_out[t * a.groups + tid] = (row_gmax[parity][tid] * inv) / 448.0f;
 
         // y / (amax_y / 448) = 448 * x*w / max|x*w|: the rsqrt cancels, so the
         // codes come straight from x*w.
@@ -391,23 +415,13 @@ fused_epilogue_kernel(EpilogueArgs a, int64_t T) {
         const Row out_q = MODE != kModeNorm ? make_row(a.quant_out + row, a.row_bytes / 2u) : out_res;
 #pragma unroll
         for (int s = 0; s < VPT; ++s) {
-            const int i = s * nthr + tid;
             float w[8], xw[8];
             unpack8(wv[s], w);
 #pragma unroll
             for (int e = 0; e < 8; ++e) xw[e] = x[s][e] * w[e];
 
-            QuantScale q = token_q;
-            float group_max = 0.0f;
-            if (MODE == kModeQuantBlock) {
-                // every lane takes part: the 16 lanes of this DPP row hold one group
-#pragma unroll
-                for (int e = 0; e < 8; ++e) group_max = fmaxf(group_max, fabsf(xw[e]));
-                group_max = row16_reduce(group_max, Max{});
-                q = quant_scale(group_max);
-            }
+            const QuantScale q = MODE == kModeQuantBlock ? quant_scale(group_max[s]) : token_q;
             // lanes past the end of the row (valid[s] false) issue no stores
-            // (the group maximum above still takes every lane of the DPP row)
             if (!valid[s]) continue;
             store16(out_res, off[s], pack_bf16x8(x[s]));
             if (a.norm_out) {
@@ -428,8 +442,6 @@ fused_epilogue_kernel(EpilogueArgs a, int64_t T) {
                 u32x2 codes = pack_e4m3x8(r);
                 if (q.qmul == 0.0f) codes = u32x2{0u, 0u};  // all-zero token or group: +0 codes
                 store8(out_q, off[s] / 2u, codes);
-                if (MODE == kModeQuantBlock && (tid & 15) == 0)
-                    a.scale_out[t * a.groups + i / 16] = (group_max * inv) / 448.0f;
             }
         }
         if (!more) break;
