@@ -29,6 +29,10 @@ int main() {
                     if (s.threads > max_threads_for(s.vpt, s.ch)) return fail("above the variant's workgroup bound", nvec, P, T, cus, s);
                     if ((long long)s.vpt * s.threads < nvec) return fail("row not covered", nvec, P, T, cus, s);
                     if (s.threads / kWave > kMaxWaves) return fail("more waves than the LDS reduction holds", nvec, P, T, cus, s);
+                    // block FP8 (rows of whole 1x128 groups): the token's scale row is
+                    // gathered in LDS and stored one lane per group
+                    if (nvec % 16 == 0 && nvec / 16 > s.threads) return fail("fewer lanes than 1x128 groups", nvec, P, T, cus, s);
+                    if (nvec % 16 == 0 && nvec / 16 > kMaxGroups) return fail("more groups than the LDS row holds", nvec, P, T, cus, s);
                     const bool persistent = T > cus && nvec >= 896 && T <= 8LL * cus;
                     if ((s.per_cu != 0) != persistent) return fail("persistent grid against the rule", nvec, P, T, cus, s);
                     if (s.per_cu != 0 && s.per_cu != 2) return fail("resident workgroups per CU", nvec, P, T, cus, s);

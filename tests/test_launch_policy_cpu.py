@@ -5,7 +5,9 @@ partials and token counts on both sides of each rule boundary, on devices of
 (vectors per lane, partials per load chunk, workgroup size within the
 variant's bound, whole waves) and cover the row, and the persistent grid must
 be chosen exactly where the rule says (rows of at least 896 vectors, more
-tokens than CUs and at most 8 per CU)."""
+tokens than CUs and at most 8 per CU). For rows of whole 1x128 groups there
+must be a lane per group and the groups must fit the LDS row that the block
+FP8 epilogue stores its scales from."""
 import os
 import shutil
 import subprocess
