@@ -398,9 +398,12 @@ fused_epilogue_kernel(EpilogueArgs a, int64_t T) {
         // One contiguous store of the token's scale row. Written a few bytes
         // per wave instead, pieces of a row whose cache lines it shares with
         // neighbouring tokens' rows (written from other XCDs) cost time at the
-        // memory side.
-        if (MODE == kModeQuantBlock && tid < a.groups)
-            a.scale_out[t * a.groups + tid] = (row_gmax[parity][tid] * inv) / 448.0f;
+        // memory side. The reduction above crosses a barrier only when the
+        // workgroup has several waves; a one-wave workgroup takes one here.
+        if (MODE == kModeQuantBlock) {
+            if (nthr == kWave) __syncthreads();
+            if (tid < a.groups) a.scale_out[t * a.groups + tid] = (row_gmax[parity][tid] * inv) / 448.0f;
+        }
 
         // y / (amax_y / 448) = 448 * x*w / max|x*w|: the rsqrt cancels, so the
         // codes come straight from x*w.
