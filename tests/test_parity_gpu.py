@@ -186,6 +186,17 @@ def test_sweep_quant_block(fn, H, P):
           label=f"block H={H} P={P}")
 
 
+@pytest.mark.parametrize("H,T", [(128, 300), (256, 1000), (512, 1000), (512, 4099)])
+def test_block_one_wave_workgroups(fn, H, T):
+    """Block FP8 on rows of at most 64 vectors with more tokens than CUs: one
+    workgroup of a single wave per token, where the token's reduction crosses
+    no barrier and the group maxima reach the scale-row store through the
+    kernel's own one-wave barrier; every row compared."""
+    inp = norm_case(T, H, 3, "quant_block", outliers=0.01, seed=H + T)
+    check(run_gpu(fn, inp, "quant_block"), run_oracle(inp, "quant_block"), "quant_block",
+          label=f"block one wave H={H} T={T}")
+
+
 @pytest.mark.parametrize("mode", list(MODES))
 @pytest.mark.parametrize("T", [1, 255, 4096])
 def test_token_counts(fn, mode, T):
