@@ -37,12 +37,16 @@ Prints ONE JSON line:
   next_rows           the further entry points, each timed alone like
                       per_config.
   token_sweep         the QK norm (local means) and the MLA epilogue at 1024 to
-                      32768 tokens, timed like per_config, with the least-
-                      squares fit us = fixed_us + bytes / (stream_GBs * 1e3):
-                      the fixed cost of a launch and its streaming rate.
+                      32768 tokens (--sweep, --sweep-tokens choose others),
+                      timed like per_config, with the least-squares fit
+                      us = fixed_us + bytes / (stream_GBs * 1e3): the fixed
+                      cost of a launch and its streaming rate.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu-baseline] [--no-next]
-                    [--no-sweep]
+                    [--no-sweep] [--sweep NAME,...] [--sweep-tokens T,...] [--sweep-only]
+
+--sweep-only prints just {"token_sweep": ...} (a measurement run, not the
+benchmark line).
 """
 import argparse
 import hashlib
@@ -85,6 +89,12 @@ def parse():
                     help="skip timing the entry points beyond the step")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the token-count sweep of the QK norm and the MLA epilogue")
+    ap.add_argument("--sweep", default=",".join(SWEEP),
+                    help="workloads of the token-count sweep (comma-separated)")
+    ap.add_argument("--sweep-tokens", default=",".join(map(str, SWEEP_TOKENS)),
+                    help="token counts of the sweep (comma-separated)")
+    ap.add_argument("--sweep-only", action="store_true",
+                    help="run only the token-count sweep and print its JSON (for profiler runs)")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
     return ap.parse_args()
 
@@ -298,25 +308,26 @@ def measure(r, torch, launches=50):
     return out
 
 
-def token_sweep(fn, wl, torch, dev):
-    """Each SWEEP workload at every SWEEP_TOKENS count, timed like per_config
-    (rotating resident copies, N launches in a graph), and the least-squares
-    line through (bytes, us): the intercept is the launch's fixed cost, the
-    slope the rate at which it streams its bytes."""
+def token_sweep(fn, wl, torch, dev, names=SWEEP, tokens=SWEEP_TOKENS):
+    """Each workload of `names` at every count of `tokens`, timed like
+    per_config (rotating resident copies, N launches in a graph), and the
+    least-squares line through (bytes, us): the intercept is the launch's
+    fixed cost, the slope the rate at which it streams its bytes."""
     out = {}
-    for name in SWEEP:
+    for name in names:
         pts = []
-        for T in SWEEP_TOKENS:
+        for T in tokens:
             r = Runner(name, fn, wl, torch, dev, T=T, quiet=True)
             n = r.sets * math.ceil(10 / r.sets)
             us = time_launches(torch, r.call, n, math.ceil(50 / n))
             pts.append({"T": T, "bytes": r.bytes, "resident_copies": r.sets, "us": round(us, 2),
                         "GB/s": round(r.bytes / us / 1e3, 1)})
+            log(f"[bench] {name} at {T} tokens: {us:.2f} us")
             del r
             torch.cuda.empty_cache()
         fixed, rate = fit_fixed_and_rate([p["bytes"] for p in pts], [p["us"] for p in pts])
         out[name] = {"points": pts, "fixed_us": round(fixed, 2), "stream_GBs": round(rate, 1)}
-        log(f"[bench] {name} over {SWEEP_TOKENS[0]}..{SWEEP_TOKENS[-1]} tokens: "
+        log(f"[bench] {name} over {tokens[0]}..{tokens[-1]} tokens: "
             f"{fixed:.2f} us fixed + bytes at {rate:.1f} GB/s")
     return out
 
@@ -439,14 +450,34 @@ def main():
               "no figure at more than one GPU.", file=sys.stderr)
         sys.exit(2)
 
+    from residual_add_rmsnorm_amd import workloads as wl
+
+    names = [n for n in args.sweep.split(",") if n]
+    bad = [n for n in names if n not in wl.WORKLOADS]
+    try:
+        tokens = [int(t) for t in args.sweep_tokens.split(",") if t]
+    except ValueError:
+        tokens = []
+    if bad or not names or not tokens or min(tokens) < 1:
+        print(f"bench.py: --sweep needs known workloads ({', '.join(wl.WORKLOADS)}) and "
+              f"--sweep-tokens positive counts (got {args.sweep!r}, {args.sweep_tokens!r})",
+              file=sys.stderr)
+        sys.exit(2)
+
     import torch
 
     from residual_add_rmsnorm_amd import fusednorm as fn
-    from residual_add_rmsnorm_amd import workloads as wl
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"[bench] {torch.cuda.get_device_name(dev)}; library {fn.library_path()}")
+    if args.sweep_only:
+        line = json.dumps({"token_sweep": token_sweep(fn, wl, torch, dev, names, tokens)})
+        if args.out:
+            with open(args.out, "w") as f:
+                f.write(line + "\n")
+        print(line, flush=True)
+        return
     runners = {n: Runner(n, fn, wl, torch, dev) for n in STEP + LATENCY}
     torch.cuda.synchronize()
     parts = [runners[n] for n in STEP]
@@ -529,7 +560,7 @@ def main():
             del r
             torch.cuda.empty_cache()
     if not args.no_sweep:
-        result["token_sweep"] = token_sweep(fn, wl, torch, dev)
+        result["token_sweep"] = token_sweep(fn, wl, torch, dev, names, tokens)
     line = json.dumps(result)
     if args.out:
         with open(args.out, "w") as f:

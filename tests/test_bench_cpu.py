@@ -1,6 +1,6 @@
-"""bench.py's host-side logic, on the CPU: the one-GPU refusal, the traffic
-figure tied to the kernel source it was measured on, and the CPU baseline's
-fields."""
+"""bench.py's host-side logic, on the CPU: the one-GPU refusal, the sweep
+options' checks, the traffic figure tied to the kernel source it was measured
+on, the CPU baseline's fields, the buffer rotation and the fixed-cost fit."""
 import json
 import os
 import subprocess
@@ -24,6 +24,15 @@ def test_more_than_one_gpu_is_refused():
                            env=dict(os.environ, **env), capture_output=True, text=True,
                            timeout=120)
         assert r.returncode == 2 and "one GPU only" in r.stderr
+        assert r.stdout == ""
+
+
+def test_sweep_arguments_are_checked_before_any_gpu_work():
+    for args in (["--sweep", "no_such_workload"], ["--sweep-tokens", "0,1024"],
+                 ["--sweep-tokens", "many"], ["--sweep", ""]):
+        r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args],
+                           capture_output=True, text=True, timeout=120)
+        assert r.returncode == 2 and "--sweep needs" in r.stderr, (args, r.stderr[-500:])
         assert r.stdout == ""
 
 
