@@ -156,11 +156,16 @@ def _partials(partials: Union[Sequence[torch.Tensor], torch.Tensor]):
     return parts, arr
 
 
+def _rows(residual: torch.Tensor):
+    """(T, H) of a [T, H] residual."""
+    if residual.dim() != 2:
+        raise ValueError(f"residual must be [T, H], got shape {tuple(residual.shape)}")
+    return residual.shape
+
+
 def _check_norm_shapes(parts, residual, weight, norm_out, residual_out, quant_out=None,
                        scale_out=None, scale_shape=None) -> None:
-    if residual.dim() != 2:
-        raise ValueError("residual must be [T, H]")
-    T, H = residual.shape
+    T, H = _rows(residual)
     for i, p in enumerate(parts):
         _shape(p, f"partials[{i}]", (T, H))
     _shape(weight, "weight", (H,))
@@ -189,7 +194,7 @@ def fused_add_rmsnorm(partials, residual: torch.Tensor, weight: torch.Tensor, ep
     parts, arr = _partials(partials)
     _need(residual, "residual")
     _need(weight, "weight")
-    T, H = residual.shape
+    T, H = _rows(residual)
     norm_out = torch.empty_like(residual) if norm_out is None else norm_out
     residual_out = torch.empty_like(residual) if residual_out is None else residual_out
     _need(norm_out, "norm_out")
@@ -211,7 +216,7 @@ def fused_add_rmsnorm_quant_fp8(partials, residual: torch.Tensor, weight: torch.
     parts, arr = _partials(partials)
     _need(residual, "residual")
     _need(weight, "weight")
-    T, H = residual.shape
+    T, H = _rows(residual)
     residual_out = torch.empty_like(residual) if residual_out is None else residual_out
     quant_out = _fp8_out(residual) if quant_out is None else quant_out
     scale_out = (torch.empty(T, dtype=torch.float32, device=residual.device)
@@ -239,7 +244,7 @@ def fused_add_rmsnorm_quant_fp8_block(partials, residual: torch.Tensor, weight: 
     parts, arr = _partials(partials)
     _need(residual, "residual")
     _need(weight, "weight")
-    T, H = residual.shape
+    T, H = _rows(residual)
     residual_out = torch.empty_like(residual) if residual_out is None else residual_out
     quant_out = _fp8_out(residual) if quant_out is None else quant_out
     if scale_out is None:
@@ -273,7 +278,7 @@ def fused_add_rmsnorm_quant_fp8_static(partials, residual: torch.Tensor, weight:
     parts, arr = _partials(partials)
     _need(residual, "residual")
     _need(weight, "weight")
-    T, H = residual.shape
+    T, H = _rows(residual)
     if not isinstance(scale_factor, torch.Tensor):
         scale_factor = torch.tensor([float(scale_factor)], dtype=torch.float32,
                                     device=residual.device)
@@ -314,7 +319,7 @@ def fused_rs_epilogue(pattern: int, partials, token_offset: int, residual: torch
     parts, arr = _partials(partials)
     _need(residual, "residual")
     _need(weight, "weight")
-    T, H = residual.shape
+    T, H = _rows(residual)
     for i, p in enumerate(parts):
         if p.dim() != 2 or p.shape[1] != H or p.shape[0] < token_offset + T or token_offset < 0:
             raise ValueError(f"partials[{i}] must be [>= token_offset + T, H]")

@@ -255,6 +255,8 @@ def test_invalid_arguments_write_nothing(fn):
         fn.fused_add_rmsnorm(parts, res, w, norm_out=parts[0], residual_out=rout)
     with pytest.raises(ValueError):                # binding refuses a short output
         fn.fused_add_rmsnorm(parts, res, w, norm_out=norm[:2], residual_out=rout)
+    with pytest.raises(ValueError, match=r"\[T, H\]"):  # a residual that is not [T, H]
+        fn.fused_add_rmsnorm_quant_fp8(parts, res.reshape(-1), w)
     torch.cuda.synchronize()
     assert torch.all(norm == 7.0) and torch.all(rout == 7.0)
 
