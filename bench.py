@@ -38,7 +38,8 @@ Prints ONE JSON line:
                       per_config.
   token_sweep         the QK norm (local means) and the MLA epilogue at 1024 to
                       32768 tokens (--sweep, --sweep-tokens choose others),
-                      timed like per_config, with the least-squares fit
+                      timed like per_config (with the mixed-stream ceiling at
+                      every count), with the least-squares fit
                       us = fixed_us + bytes / (stream_GBs * 1e3): the fixed
                       cost of a launch and its streaming rate.
 
@@ -310,9 +311,10 @@ def measure(r, torch, launches=50):
 
 def token_sweep(fn, wl, torch, dev, names=SWEEP, tokens=SWEEP_TOKENS):
     """Each workload of `names` at every count of `tokens`, timed like
-    per_config (rotating resident copies, N launches in a graph), and the
-    least-squares line through (bytes, us): the intercept is the launch's
-    fixed cost, the slope the rate at which it streams its bytes."""
+    per_config (rotating resident copies, N launches in a graph) beside its
+    mixed-stream ceiling on the same buffers, and the least-squares line
+    through (bytes, us): the intercept is the launch's fixed cost, the slope
+    the rate at which it streams its bytes."""
     out = {}
     for name in names:
         pts = []
@@ -320,9 +322,13 @@ def token_sweep(fn, wl, torch, dev, names=SWEEP, tokens=SWEEP_TOKENS):
             r = Runner(name, fn, wl, torch, dev, T=T, quiet=True)
             n = r.sets * math.ceil(10 / r.sets)
             us = time_launches(torch, r.call, n, math.ceil(50 / n))
+            mix_us = time_launches(torch, r.mix, n, math.ceil(50 / n))
             pts.append({"T": T, "bytes": r.bytes, "resident_copies": r.sets, "us": round(us, 2),
-                        "GB/s": round(r.bytes / us / 1e3, 1)})
-            log(f"[bench] {name} at {T} tokens: {us:.2f} us")
+                        "GB/s": round(r.bytes / us / 1e3, 1),
+                        "mixed_ceiling_us": round(mix_us, 2),
+                        "mixed_ceiling_GBs": round(r.mix_bytes / mix_us / 1e3, 1)})
+            log(f"[bench] {name} at {T} tokens: {us:.2f} us; same bytes, no arithmetic: "
+                f"{mix_us:.2f} us")
             del r
             torch.cuda.empty_cache()
         fixed, rate = fit_fixed_and_rate([p["bytes"] for p in pts], [p["us"] for p in pts])
